@@ -1,0 +1,147 @@
+"""Planted mistakes in the oracle (CPU only): each must be caught by the pins.
+
+Each mutant replaces one oracle routine with a plausible wrong variant (a
+dropped term, a wrong sign or index, an inclusive instead of exclusive
+prefix, another rounding).  The pin suite is then run against the mutated
+oracle and must fail.  This shows the pins are sharp enough to catch that
+class of error; the real oracle passes the same suite in test_oracle_pins.py.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from oracle import numerics as N
+from tests import test_oracle_pins as P
+
+
+def _pin_suite():
+    P.test_golden_layout_dispatch_combine()
+    P.test_golden_fp8_blocks()
+    P.test_golden_combine_fp32_order()
+    for case in P.TINY_CASES[:5]:
+        for dtype in ("bf16", "fp8"):
+            P.test_oracle_vs_bruteforce(case, dtype)
+    P.test_fp8_edge_rows()
+    P.test_identity_round_trip_k1_is_exact()
+    P.test_identity_round_trip_weighted(P.W.CONFIG_BY_NAME["tiny"])
+
+
+def _rank_modulo(topk_idx, E, R):
+    e = topk_idx.astype(np.int64)
+    valid = (e >= 0) & (e < E)
+    return valid, np.where(valid, e % R, -1)
+
+
+def _slots_inclusive(mask):
+    m = mask.astype(np.int64) != 0
+    offs = np.zeros(m.shape[1] + 1, dtype=np.int64)
+    offs[1:] = np.cumsum(m.sum(axis=0))
+    send = np.where(m, offs[None, :-1] + np.cumsum(m, axis=0), -1)
+    return offs.astype(np.int32), send.astype(np.int32), int(offs[-1])
+
+
+def _slots_descending(mask):
+    m = mask.astype(np.int64) != 0
+    offs = np.zeros(m.shape[1] + 1, dtype=np.int64)
+    offs[1:] = np.cumsum(m.sum(axis=0))
+    after = np.cumsum(m[::-1], axis=0)[::-1] - m
+    send = np.where(m, offs[None, :-1] + after, -1)
+    return offs.astype(np.int32), send.astype(np.int32), int(offs[-1])
+
+
+def _bf16_truncate(x):
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _e4m3_ties_away(x):
+    v = np.ascontiguousarray(x, dtype=np.float32)
+    a = np.abs(v).astype(np.float64)
+    t = N.E4M3_MAGNITUDES
+    hi = np.minimum(np.searchsorted(t, a), 126)
+    lo = np.maximum(hi - 1, 0)
+    code = np.where(t[hi] - a <= a - t[lo], hi, lo)
+    code = np.where(a >= 448.0, 126, code)
+    return (code | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def _quant_reciprocal(x_bits):
+    rows, H = x_bits.shape
+    x = N.bf16_bits_to_f32(x_bits).reshape(rows, H // 128, 128)
+    a = np.maximum(np.abs(x).max(axis=2), np.float32(1e-4))
+    s = (a / np.float32(448)).astype(np.float32)
+    v = (x * (np.float32(448) / a)[:, :, None]).astype(np.float32)
+    return N.e4m3_encode_rne(v).reshape(rows, H), s
+
+
+def _quant_no_floor(x_bits):
+    rows, H = x_bits.shape
+    x = N.bf16_bits_to_f32(x_bits).reshape(rows, H // 128, 128)
+    a = np.abs(x).max(axis=2)
+    s = (a / np.float32(448)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        v = (x / s[:, :, None]).astype(np.float32)
+    v = np.nan_to_num(v)
+    return N.e4m3_encode_rne(v).reshape(rows, H), s
+
+
+_orig_combine = O.combine
+
+
+def _combine_drop_last(y, idx, w, send_row, E, R, tokens=None):
+    return _orig_combine(y, idx[:, :-1], w[:, :-1], send_row, E, R, tokens)
+
+
+def _combine_fp64(y, idx, w, send_row, E, R, tokens=None):
+    acc, _ = O.combine_f64(y, idx, w, send_row, E, R, tokens)
+    return N.f32_to_bf16_bits_rne(acc.astype(np.float32))
+
+
+def _combine_fused(y, idx, w, send_row, E, R, tokens=None):
+    valid, rank = O.expert_ranks(idx, E, R)
+    t_sel = np.arange(idx.shape[0]) if tokens is None else np.asarray(tokens)
+    acc = np.zeros((t_sel.size, y.shape[1]), dtype=np.float32)
+    for j in range(idx.shape[1]):
+        ok = valid[t_sel, j]
+        tj = t_sel[ok]
+        rows = send_row[tj, rank[tj, j]]
+        exact = w[tj, j][:, None].astype(np.float64) * N.bf16_bits_to_f32(y[rows]).astype(np.float64)
+        acc[ok] = (acc[ok].astype(np.float64) + exact).astype(np.float32)
+    return N.f32_to_bf16_bits_rne(acc)
+
+
+def _combine_reversed(y, idx, w, send_row, E, R, tokens=None):
+    return _orig_combine(y, idx[:, ::-1].copy(), w[:, ::-1].copy(), send_row, E, R, tokens)
+
+
+_orig_meta = O.dispatch_metadata
+
+
+def _meta_global_ids(idx, w, E, R, send_row, n):
+    src, ridx, rw = _orig_meta(idx, w, E, R, send_row, n)
+    L = E // R
+    rows_rank = np.searchsorted(np.cumsum((send_row >= 0).sum(axis=0)), np.arange(n), side="right")
+    return src, np.where(ridx >= 0, ridx + rows_rank[:, None] * L, -1).astype(np.int32), rw
+
+
+MUTANTS = {
+    "rank_is_e_mod_R": ("expert_ranks", _rank_modulo),
+    "inclusive_prefix": ("assign_slots", _slots_inclusive),
+    "descending_tokens_in_segment": ("assign_slots", _slots_descending),
+    "bf16_truncation": ("f32_to_bf16_bits_rne", _bf16_truncate),
+    "e4m3_ties_away_from_zero": ("e4m3_encode_rne", _e4m3_ties_away),
+    "fp8_multiply_by_reciprocal": ("quantize_fp8_blocks", _quant_reciprocal),
+    "fp8_no_amax_floor": ("quantize_fp8_blocks", _quant_no_floor),
+    "combine_drops_last_slot": ("combine", _combine_drop_last),
+    "combine_fp64_accumulate": ("combine", _combine_fp64),
+    "combine_reversed_slot_order": ("combine", _combine_reversed),
+    "combine_fused_multiply_add": ("combine", _combine_fused),
+    "metadata_global_expert_ids": ("dispatch_metadata", _meta_global_ids),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    with pytest.raises(AssertionError):
+        _pin_suite()
