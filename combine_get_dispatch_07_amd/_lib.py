@@ -1,0 +1,157 @@
+"""ctypes binding of libmoe_ep.so (the C ABI in include/moe_ep.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype,
+contiguity and size against the shape, then their device pointers and the
+current HIP stream are handed to the library.  Every step of the path runs in
+the library's HIP kernels; there is no fallback.  Importing this module loads
+the library and raises if it has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_CAPACITY = 2
+MOE_ERR_UNSUPPORTED = 3
+MOE_ERR_HIP = 4
+
+MOE_BF16 = 0
+MOE_FP8_E4M3 = 1
+DTYPES = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+
+
+class MoeShapeC(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("num_topk", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("num_ranks", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class MoeShape:
+    num_tokens: int
+    hidden: int
+    num_topk: int
+    num_experts: int
+    num_ranks: int
+
+    def c(self) -> MoeShapeC:
+        return MoeShapeC(self.num_tokens, self.hidden, self.num_topk, self.num_experts, self.num_ranks)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {status_string(code)} ({code})")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m combine_get_dispatch_07_amd.build` "
+                          "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    SH = ctypes.POINTER(MoeShapeC)
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_workspace_bytes.argtypes = [SH]
+    lib.moe_workspace_bytes.restype = SZ
+    lib.moe_max_recv_rows.argtypes = [SH]
+    lib.moe_max_recv_rows.restype = I32
+    lib.moe_get_dispatch_layout.argtypes = [SH, P, P, P, P, P, SZ, P]
+    lib.moe_get_dispatch_layout.restype = ctypes.c_int
+    lib.moe_dispatch.argtypes = [SH, ctypes.c_int, P, P, P, P, SZ, I32, P, P, P, P, P, P, P, P, P]
+    lib.moe_dispatch.restype = ctypes.c_int
+    lib.moe_combine.argtypes = [SH, P, I32, P, P, P, P, P]
+    lib.moe_combine.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def status_string(code: int) -> str:
+    return lib.moe_status_string(int(code)).decode()
+
+
+def workspace_bytes(shape: MoeShape) -> int:
+    return int(lib.moe_workspace_bytes(ctypes.byref(shape.c())))
+
+
+def max_recv_rows(shape: MoeShape) -> int:
+    return int(lib.moe_max_recv_rows(ctypes.byref(shape.c())))
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype, numel: Optional[int] = None) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _check(fn: str, code: int) -> None:
+    if code != MOE_OK:
+        raise MoeError(fn, code)
+
+
+def moe_get_dispatch_layout(shape: MoeShape, topk_idx, tokens_per_rank, tokens_per_expert, is_token_in_rank,
+                            workspace, stream=None) -> None:
+    T, k, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
+    code = lib.moe_get_dispatch_layout(
+        ctypes.byref(shape.c()), _ptr(topk_idx, "topk_idx", torch.int32, T * k),
+        _ptr(tokens_per_rank, "tokens_per_rank", torch.int32, R),
+        _ptr(tokens_per_expert, "tokens_per_expert", torch.int32, E),
+        _ptr(is_token_in_rank, "is_token_in_rank", torch.uint8, T * R),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check("moe_get_dispatch_layout", code)
+
+
+def moe_dispatch(shape: MoeShape, dtype: str, x, topk_idx, topk_w, workspace, recv_x, recv_scales, recv_src_idx,
+                 recv_topk_idx, recv_topk_w, rank_offsets, send_row, num_recv, stream=None) -> None:
+    T, H, k, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
+    fp8 = DTYPES[dtype] == MOE_FP8_E4M3
+    cap = recv_src_idx.numel()
+    code = lib.moe_dispatch(
+        ctypes.byref(shape.c()), DTYPES[dtype], _ptr(x, "x", torch.bfloat16, T * H),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), cap,
+        _ptr(recv_x, "recv_x", torch.uint8 if fp8 else torch.bfloat16, cap * H),
+        _ptr(recv_scales, "recv_scales", torch.float32, cap * (H // 128)) if fp8 else None,
+        _ptr(recv_src_idx, "recv_src_idx", torch.int32, cap),
+        _ptr(recv_topk_idx, "recv_topk_idx", torch.int32, cap * k),
+        _ptr(recv_topk_w, "recv_topk_w", torch.float32, cap * k),
+        _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),
+        _ptr(send_row, "send_row", torch.int32, T * R), _ptr(num_recv, "num_recv", torch.int32, 1),
+        _stream(stream))
+    _check("moe_dispatch", code)
+
+
+def moe_combine(shape: MoeShape, y, topk_idx, topk_w, send_row, out, stream=None, num_y_rows=None) -> None:
+    T, H, k, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
+    rows = y.shape[0] if num_y_rows is None else int(num_y_rows)
+    code = lib.moe_combine(
+        ctypes.byref(shape.c()), _ptr(y, "y", torch.bfloat16, rows * H), rows,
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
+        _ptr(send_row, "send_row", torch.int32, T * R), _ptr(out, "out", torch.bfloat16, T * H), _stream(stream))
+    _check("moe_combine", code)

@@ -1,0 +1,70 @@
+"""Build libmoe_ep.so (the C-ABI library) for gfx950 with hipcc, in-tree.
+
+    python -m combine_get_dispatch_07_amd.build        # or __graft_entry__.build()
+
+Flags that matter for results:
+* ``-ffp-contract=off`` (plus ``#pragma clang fp contract(off)`` in the
+  kernels): combine multiplies then adds, never a fused multiply-add.
+* ``-fhip-fp32-correctly-rounded-divide-sqrt``: the FP8 scale and the x / s
+  quotients are IEEE correctly rounded divisions.
+* ``-target-feature -packed-fp32-ops``: no packed fp32 instructions.
+* fp32 denormals are kept (no flush-to-zero flag).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from typing import Iterable, Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+SRC = os.path.join(PKG_DIR, "csrc", "moe_ep.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libmoe_ep.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-ffp-contract=off",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+    return path
+
+
+def build(out: Optional[str] = None, defines: Iterable[str] = (), extra_flags: Iterable[str] = (),
+          verbose: bool = False) -> str:
+    """Compile the library; returns the path of the built .so."""
+    out = out or LIB_PATH
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", *[f"-D{d}" for d in defines], *extra_flags,
+           SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    errs = "\n".join(l for l in res.stderr.splitlines() if noise not in l and "ignoring feature" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
+    if verbose and errs.strip():
+        print(errs, file=sys.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

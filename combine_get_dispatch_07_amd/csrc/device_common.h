@@ -1,0 +1,64 @@
+// Device helpers shared by the layout, dispatch and combine kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Rank owning expert e: floor(e / L), computed as (e * ceil(2^32 / L)) >> 32.
+// Exact for e, L < 2^16 (the error term e * (magic * L - 2^32) stays below 2^32).
+__device__ __forceinline__ int rank_of(int e, uint64_t magic) {
+  return (int)(((uint64_t)(uint32_t)e * magic) >> 32);
+}
+
+// 64-bit value of `lane` in a wave-uniform (scalar) register pair.
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int u = __shfl_up(v, d, kWave);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// bf16 halves of a 32-bit word, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// fp32 -> OCP E4M3 ("fn": bias 7, max 448, no infinities) code, round to nearest
+// even, sign kept.  Magnitudes from 464 up saturate to 448 (RNE already maps
+// [448, 464] to 448), which the per-block scaling never exceeds.
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  // normal range: keep 3 mantissa bits, round the other 20 to nearest even,
+  // then move the exponent bias from 127 to 7 (a carry rolls into the exponent)
+  const uint32_t rounded = a + 0x7ffffu + ((a >> 20) & 1u);
+  const uint32_t normal = (rounded >> 20) - (120u << 3);
+  // below 2^-6: multiples of 2^-9; a * 512 is exact and rint rounds ties to even
+  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  uint32_t code = a < 0x3c800000u ? sub : normal;
+  code = a >= 0x43e80000u ? 0x7eu : code;
+  return sign | code;
+}
+
+}  // namespace moe

@@ -1,0 +1,181 @@
+// Dispatch kernel: stable prefix-sum slot assignment plus the row pack, bf16
+// bit copy or FP8 E4M3 with one fp32 scale per 128 channels.
+//
+// Follows "DeepEP：年度总结中的计算通信重叠摘记" (notes.kuangjux.top), section
+// 节点内通信 (rows go only to ranks in is_token_in_rank; FP8 halves the bytes
+// moved), and the mlqm.cn rocSHMEM notes, section 3.2 (rows are packed into a
+// preallocated receive buffer).  Receive row of (t, r) = rank_offsets[r] +
+// #{t' < t : t' goes to r}: segments in rank order, tokens ascending.
+//
+// Work item = (token, hidden slice); one wave per item.  A wave reads the
+// 64 rank bitmasks of its token's chunk (one per lane); a ballot per
+// destination rank plus the chunk's precomputed base gives the row.  The
+// slice is loaded once with 16-byte loads (each instruction reads 1 KiB
+// contiguous), quantised once if FP8, and stored to every destination row
+// with nontemporal stores (the receive rows are not re-read by this kernel).
+#pragma once
+
+#include "device_common.h"
+
+namespace moe {
+
+constexpr int kDispatchBlock = 256;  // 4 waves, 4 work items per block
+constexpr int kFp8Block = 128;       // channels per FP8 scale
+constexpr float kAmaxFloor = 1e-4f;
+constexpr float kE4m3Max = 448.0f;
+
+struct DispatchArgs {
+  const uint16_t* x;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const uint64_t* token_ranks;
+  const int32_t* chunk_base;
+  const int32_t* ws_rank_offsets;
+  void* recv_x;
+  float* recv_scales;
+  int32_t* recv_src_idx;
+  int32_t* recv_topk_idx;
+  float* recv_topk_w;
+  int32_t* rank_offsets;
+  int32_t* send_row;
+  int32_t* num_recv;
+  uint64_t rank_magic;
+  uint64_t rank_bits;  // (1 << R) - 1
+  int T, H, H8, k, E, R, L, NC;
+  int capacity;  // receive rows allocated; rows at or beyond it are never written
+  int slices;    // hidden slices per token
+  int items;   // T * slices
+};
+
+// Eight bf16 channels of one lane -> eight E4M3 codes, given the block scale.
+__device__ __forceinline__ u32x2 quantize8(u32x4 v, float s) {
+#pragma clang fp contract(off)
+  uint32_t q[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q[2 * i] = e4m3_rne(bf16_lo(v[i]) / s);
+    q[2 * i + 1] = e4m3_rne(bf16_hi(v[i]) / s);
+  }
+  u32x2 out;
+  out[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+  out[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+  return out;
+}
+
+// |x| maximum over the 16 lanes (128 channels) sharing a scale, as fp32.
+__device__ __forceinline__ float block_amax(u32x4 v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = max(m, v[i] & 0x7fffu);
+    m = max(m, (v[i] >> 16) & 0x7fffu);
+  }
+  // bf16 magnitudes order like their bit patterns, so the maximum is exact
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 4, kWave));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 8, kWave));
+  return __uint_as_float(m << 16);
+}
+
+template <int U, bool kFp8>
+__global__ __launch_bounds__(kDispatchBlock) void dispatch_kernel(DispatchArgs a) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x * (kDispatchBlock / kWave) + wave;
+
+  if (blockIdx.x == 0 && wave == 0) {  // publish the segment offsets and the row count
+    if (lane < a.R) a.rank_offsets[lane] = a.ws_rank_offsets[lane];
+    if (lane == 0) {
+      a.rank_offsets[a.R] = a.ws_rank_offsets[a.R];
+      *a.num_recv = a.ws_rank_offsets[a.R];
+    }
+  }
+  if (item >= a.items) return;
+
+  const int t = item / a.slices;
+  const int s = item - t * a.slices;
+  const int chunk = t >> 6;
+  const int tl = t & (kWave - 1);
+
+  // Rank bitmasks of the chunk's 64 tokens, one per lane; this token's is uniform.
+  const int tt = (chunk << 6) + lane;
+  const uint64_t lm = tt < a.T ? a.token_ranks[tt] : 0ull;
+  const uint64_t mine = readlane64(lm, tl) & a.rank_bits;
+  const uint64_t lanes_below = tl == 0 ? 0ull : (~0ull >> (kWave - tl));
+
+  // Load this lane's U 16-byte pieces of the slice (8 bf16 channels each).
+  const int c0 = s * (U * kWave) + lane;
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H);
+  u32x4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = c0 + u * kWave;
+    v[u] = c < a.H8 ? __builtin_nontemporal_load(xrow + c) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  u32x2 q[U];
+  float sc[U];
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float amax = block_amax(v[u]);
+      sc[u] = fmaxf(amax, kAmaxFloor) / kE4m3Max;
+      q[u] = quantize8(v[u], sc[u]);
+    }
+  }
+
+  // Slot metadata: lane j < k holds slot j of this token.
+  const bool meta = s == 0;
+  int ej = -1, rj = -1;
+  float wj = 0.0f;
+  if (meta && lane < a.k) {
+    ej = a.topk_idx[(size_t)t * a.k + lane];
+    wj = a.topk_w[(size_t)t * a.k + lane];
+    if ((unsigned)ej < (unsigned)a.E) rj = rank_of(ej, a.rank_magic);
+  }
+
+  int my_row = -1;  // lane r: receive row of (t, r)
+  uint64_t todo = mine;
+  while (todo) {
+    const int r = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const uint64_t before = __ballot((lm >> r) & 1ull) & lanes_below;
+    const int row = a.ws_rank_offsets[r] + a.chunk_base[r * a.NC + chunk] + __popcll(before);
+    if ((unsigned)row >= (unsigned)a.capacity) continue;  // only a plan from another layout gets here
+    my_row = lane == r ? row : my_row;
+
+    if constexpr (kFp8) {
+      u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.recv_x) + (size_t)row * a.H);
+      float* sdst = a.recv_scales + (size_t)row * (a.H / kFp8Block);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * kWave;
+        if (c < a.H8) {
+          __builtin_nontemporal_store(q[u], dst + c);
+          if ((lane & 15) == 0) sdst[c >> 4] = sc[u];
+        }
+      }
+    } else {
+      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.recv_x) + (size_t)row * a.H);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * kWave;
+        if (c < a.H8) __builtin_nontemporal_store(v[u], dst + c);
+      }
+    }
+
+    if (meta) {
+      if (lane == 0) a.recv_src_idx[row] = t;
+      if (lane < a.k) {
+        const int local = rj == r ? ej - r * a.L : -1;
+        a.recv_topk_idx[(size_t)row * a.k + lane] = local;
+        a.recv_topk_w[(size_t)row * a.k + lane] = local >= 0 ? wj : 0.0f;
+      }
+    }
+  }
+  if (meta && lane < a.R) a.send_row[(size_t)t * a.R + lane] = my_row;
+}
+
+}  // namespace moe

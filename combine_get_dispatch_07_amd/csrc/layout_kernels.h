@@ -1,0 +1,165 @@
+// Dispatch layout kernels: top-k expert ids -> is_token_in_rank, per-rank and
+// per-expert token counts, and the dispatch plan (per-token rank bitmask and
+// per-64-token-chunk exclusive prefix counts per rank).
+//
+// Follows the is_token_in_rank filter of "DeepEP：年度总结中的计算通信重叠摘记"
+// (notes.kuangjux.top), section 节点内通信: a token is marked only for the
+// ranks that own one of its top-k experts.
+//
+// One lane per token, one wave per 64-token chunk.  Per-rank chunk counts come
+// from wave ballots (one ballot + popcount per rank), expert counts from an
+// LDS histogram; all counting is integer, so results do not depend on
+// scheduling.  Inter-block prefix sums are done by a second, single-block
+// kernel rather than by blocks waiting on each other.
+#pragma once
+
+#include "device_common.h"
+
+namespace moe {
+
+constexpr int kLayoutBlock = 256;      // tokens per block, multi-block path
+constexpr int kFusedMaxTokens = 1024;  // up to this many tokens: one block does everything
+constexpr int kFusedMaxChunks = kFusedMaxTokens / kWave;
+
+struct LayoutArgs {
+  const int32_t* topk_idx;
+  int32_t* tokens_per_rank;
+  int32_t* tokens_per_expert;
+  uint8_t* mask;           // [T, R] bytes
+  uint64_t* token_ranks;   // plan: [T] rank bitmask
+  int32_t* chunk_base;     // plan: [R, NC] chunk counts, then exclusive prefix per rank
+  int32_t* block_expert;   // plan scratch: [NB, E] per-block expert histogram
+  int32_t* ws_rank_offsets;// plan: [R + 1]
+  uint64_t rank_magic;
+  int T, k, E, R, NC, NB;
+  int mask_words;          // 1: mask rows written as 32-bit words (R % 4 == 0, aligned)
+};
+
+// Rank bitmask of token t; valid expert ids are added to the LDS histogram.
+__device__ __forceinline__ uint64_t token_rank_mask(const LayoutArgs& a, int t, int* hist) {
+  uint64_t m = 0;
+  if (t < a.T) {
+    const int32_t* row = a.topk_idx + (size_t)t * a.k;
+    for (int j = 0; j < a.k; ++j) {
+      const int e = row[j];
+      if ((unsigned)e < (unsigned)a.E) {
+        m |= 1ull << rank_of(e, a.rank_magic);
+        atomicAdd(&hist[e], 1);
+      }
+    }
+  }
+  return m;
+}
+
+__device__ __forceinline__ void write_mask_row(const LayoutArgs& a, int t, uint64_t m) {
+  uint8_t* dst = a.mask + (size_t)t * a.R;
+  if (a.mask_words) {
+    uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+    for (int w = 0; w < (a.R >> 2); ++w) {
+      const uint32_t b = (uint32_t)(m >> (4 * w)) & 0xfu;
+      d32[w] = (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
+    }
+  } else {
+    for (int r = 0; r < a.R; ++r) dst[r] = (uint8_t)((m >> r) & 1u);
+  }
+}
+
+// Lane r (< R) returns how many lanes of the wave have bit r set in m.
+__device__ __forceinline__ int wave_rank_counts(uint64_t m, int R, int lane) {
+  int mine = 0;
+  for (int r = 0; r < R; ++r) {
+    const int c = __popcll(__ballot((m >> r) & 1ull));
+    mine = lane == r ? c : mine;
+  }
+  return mine;
+}
+
+// Wave 0: per-rank totals -> tokens_per_rank and the exclusive rank offsets.
+__device__ __forceinline__ void publish_rank_offsets(const LayoutArgs& a, const int* total, int lane) {
+  const int v = lane < a.R ? total[lane] : 0;
+  const int incl = wave_inclusive_scan(v, lane);
+  if (lane < a.R) {
+    a.tokens_per_rank[lane] = v;
+    a.ws_rank_offsets[lane] = incl - v;
+  }
+  if (lane == a.R - 1) a.ws_rank_offsets[a.R] = incl;
+}
+
+// T <= kFusedMaxTokens: a single block of ceil(T/64) waves (at least one).
+__global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArgs a) {
+  extern __shared__ int hist[];  // [E]
+  __shared__ int chunk_cnt[kWave * kFusedMaxChunks];  // [R][16]
+  __shared__ int rank_total[kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  for (int e = tid; e < a.E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+
+  const uint64_t m = token_rank_mask(a, tid, hist);
+  if (tid < a.T) {
+    a.token_ranks[tid] = m;
+    write_mask_row(a, tid, m);
+  }
+  const int cnt = wave_rank_counts(m, a.R, lane);
+  if (lane < a.R) chunk_cnt[lane * kFusedMaxChunks + wave] = cnt;
+  __syncthreads();
+
+  for (int e = tid; e < a.E; e += blockDim.x) a.tokens_per_expert[e] = hist[e];
+  if (tid < a.R) {
+    int run = 0;
+    for (int c = 0; c < a.NC; ++c) {
+      a.chunk_base[tid * a.NC + c] = run;
+      run += chunk_cnt[tid * kFusedMaxChunks + c];
+    }
+    rank_total[tid] = run;
+  }
+  __syncthreads();
+  if (wave == 0) publish_rank_offsets(a, rank_total, lane);
+}
+
+// Multi-block path, pass 1: mask rows, token bitmasks, chunk counts, block histograms.
+__global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a) {
+  extern __shared__ int hist[];  // [E]
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  for (int e = tid; e < a.E; e += kLayoutBlock) hist[e] = 0;
+  __syncthreads();
+
+  const int t = blockIdx.x * kLayoutBlock + tid;
+  const uint64_t m = token_rank_mask(a, t, hist);
+  if (t < a.T) {
+    a.token_ranks[t] = m;
+    write_mask_row(a, t, m);
+  }
+  const int chunk = t >> 6;
+  const int cnt = wave_rank_counts(m, a.R, lane);
+  if (chunk < a.NC && lane < a.R) a.chunk_base[lane * a.NC + chunk] = cnt;
+  __syncthreads();
+  for (int e = tid; e < a.E; e += kLayoutBlock) a.block_expert[(size_t)blockIdx.x * a.E + e] = hist[e];
+}
+
+// Multi-block path, pass 2 (one block): expert totals, per-rank chunk prefix, rank offsets.
+__global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutArgs a) {
+  __shared__ int rank_total[kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+  for (int e = tid; e < a.E; e += blockDim.x) {
+    int s = 0;
+    for (int b = 0; b < a.NB; ++b) s += a.block_expert[(size_t)b * a.E + e];
+    a.tokens_per_expert[e] = s;
+  }
+  for (int r = wave; r < a.R; r += nwaves) {
+    int* row = a.chunk_base + (size_t)r * a.NC;
+    int carry = 0;
+    for (int c0 = 0; c0 < a.NC; c0 += kWave) {
+      const int c = c0 + lane;
+      const int v = c < a.NC ? row[c] : 0;
+      const int incl = wave_inclusive_scan(v, lane);
+      if (c < a.NC) row[c] = carry + incl - v;
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) rank_total[r] = carry;
+  }
+  __syncthreads();
+  if (wave == 0) publish_rank_offsets(a, rank_total, lane);
+}
+
+}  // namespace moe

@@ -1,0 +1,294 @@
+// Host side of the C ABI declared in include/moe_ep.h: argument checks, the
+// workspace (dispatch plan) carve-up, launch shapes and kernel launches.
+// Everything is checked before the first HIP call, so a rejected call touches
+// neither the GPU nor any memory.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "moe_ep.h"
+
+#include "combine_kernels.h"
+#include "device_common.h"
+#include "dispatch_kernels.h"
+#include "layout_kernels.h"
+
+namespace {
+
+constexpr int kMaxTopk = 32;
+constexpr int kMaxRanks = 64;
+constexpr int kMaxExperts = 4096;
+constexpr size_t kPlanAlign = 256;
+// Enough waves to keep every SIMD of the 256 CUs busy several times over.
+constexpr long kTargetWaves = 8192;
+
+struct PlanLayout {
+  size_t token_ranks, chunk_base, block_expert, rank_offsets, total;
+  int NC, NB;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+moe_status check_shape(const moe_shape* s) {
+  if (s == nullptr) return MOE_ERR_INVALID_ARG;
+  const int64_t T = s->num_tokens, H = s->hidden, k = s->num_topk, E = s->num_experts,
+                R = s->num_ranks;
+  if (T < 0 || H <= 0 || H % 8 != 0 || k < 1 || E < 1 || R < 1) return MOE_ERR_INVALID_ARG;
+  if (k > kMaxTopk || R > kMaxRanks || E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (R > E || E % R != 0 || k > E) return MOE_ERR_INVALID_ARG;
+  if (T * k > INT32_MAX || T * R > INT32_MAX || T * std::min(k, R) > INT32_MAX)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+PlanLayout plan_layout(const moe_shape& s) {
+  PlanLayout p{};
+  const size_t T = (size_t)s.num_tokens, R = (size_t)s.num_ranks, E = (size_t)s.num_experts;
+  p.NC = (int)((T + moe::kWave - 1) / moe::kWave);
+  p.NB = (int)((T + moe::kLayoutBlock - 1) / moe::kLayoutBlock);
+  size_t off = 0;
+  p.token_ranks = off;
+  off = align_up(off + T * sizeof(uint64_t), kPlanAlign);
+  p.chunk_base = off;
+  off = align_up(off + R * (size_t)p.NC * sizeof(int32_t), kPlanAlign);
+  p.block_expert = off;
+  off = align_up(off + (size_t)p.NB * E * sizeof(int32_t), kPlanAlign);
+  p.rank_offsets = off;
+  off = align_up(off + (R + 1) * sizeof(int32_t), kPlanAlign);
+  p.total = off;
+  return p;
+}
+
+uint64_t rank_magic(const moe_shape& s) {
+  const uint64_t L = (uint64_t)(s.num_experts / s.num_ranks);
+  return ((1ull << 32) + L - 1) / L;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Chunks of 8 channels per lane per work item, from the instantiated set.
+// Fewer, wider items amortise the per-item slot arithmetic; narrower ones
+// give small batches enough waves to fill the chip.
+int pick_chunks_per_lane(int T, int H8) {
+  static const int kOptions[] = {14, 7, 4, 2, 1};
+  const int groups = (H8 + moe::kWave - 1) / moe::kWave;  // 64-lane chunk groups per row
+  for (int u : kOptions) {
+    if (u > groups) continue;
+    const long slices = (groups + u - 1) / u;
+    if ((long)T * slices >= kTargetWaves) return u;
+  }
+  return 1;
+}
+
+moe_status last_launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+template <bool kFp8>
+void launch_dispatch(int U, dim3 grid, hipStream_t stream, const moe::DispatchArgs& a) {
+  const dim3 block(moe::kDispatchBlock);
+  switch (U) {
+    case 14: hipLaunchKernelGGL((moe::dispatch_kernel<14, kFp8>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((moe::dispatch_kernel<7, kFp8>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((moe::dispatch_kernel<4, kFp8>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((moe::dispatch_kernel<2, kFp8>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((moe::dispatch_kernel<1, kFp8>), grid, block, 0, stream, a); break;
+  }
+}
+
+void launch_combine(int U, dim3 grid, hipStream_t stream, const moe::CombineArgs& a) {
+  const dim3 block(moe::kCombineBlock);
+  switch (U) {
+    case 4: hipLaunchKernelGGL((moe::combine_kernel<4>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((moe::combine_kernel<2>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((moe::combine_kernel<1>), grid, block, 0, stream, a); break;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_CAPACITY: return "MOE_ERR_CAPACITY";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return plan_layout(*shape).total;
+}
+
+int32_t moe_max_recv_rows(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return -1;
+  return shape->num_tokens * std::min(shape->num_topk, shape->num_ranks);
+}
+
+moe_status moe_get_dispatch_layout(const moe_shape* shape, const int32_t* topk_idx,
+                                   int32_t* tokens_per_rank, int32_t* tokens_per_expert,
+                                   uint8_t* is_token_in_rank, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape s = *shape;
+  if (!topk_idx || !tokens_per_rank || !tokens_per_expert || !is_token_in_rank || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(topk_idx, 4) || !aligned(tokens_per_rank, 4) || !aligned(tokens_per_expert, 4) ||
+      !aligned(workspace, kPlanAlign))
+    return MOE_ERR_INVALID_ARG;
+  const PlanLayout p = plan_layout(s);
+  if (workspace_bytes < p.total) return MOE_ERR_INVALID_ARG;
+
+  char* ws = static_cast<char*>(workspace);
+  moe::LayoutArgs a{};
+  a.topk_idx = topk_idx;
+  a.tokens_per_rank = tokens_per_rank;
+  a.tokens_per_expert = tokens_per_expert;
+  a.mask = is_token_in_rank;
+  a.token_ranks = reinterpret_cast<uint64_t*>(ws + p.token_ranks);
+  a.chunk_base = reinterpret_cast<int32_t*>(ws + p.chunk_base);
+  a.block_expert = reinterpret_cast<int32_t*>(ws + p.block_expert);
+  a.ws_rank_offsets = reinterpret_cast<int32_t*>(ws + p.rank_offsets);
+  a.rank_magic = rank_magic(s);
+  a.T = s.num_tokens;
+  a.k = s.num_topk;
+  a.E = s.num_experts;
+  a.R = s.num_ranks;
+  a.NC = p.NC;
+  a.NB = p.NB;
+  a.mask_words = (s.num_ranks % 4 == 0 && aligned(is_token_in_rank, 4)) ? 1 : 0;
+  const size_t hist_bytes = (size_t)s.num_experts * sizeof(int);
+
+  if (s.num_tokens <= moe::kFusedMaxTokens) {
+    const int threads = std::max(moe::kWave, (s.num_tokens + moe::kWave - 1) / moe::kWave * moe::kWave);
+    hipLaunchKernelGGL(moe::layout_fused_kernel, dim3(1), dim3(threads), hist_bytes, stream, a);
+  } else {
+    hipLaunchKernelGGL(moe::layout_count_kernel, dim3(p.NB), dim3(moe::kLayoutBlock), hist_bytes,
+                       stream, a);
+    hipLaunchKernelGGL(moe::layout_finalize_kernel, dim3(1), dim3(1024), 0, stream, a);
+  }
+  return last_launch_status();
+}
+
+moe_status moe_dispatch(const moe_shape* shape, moe_dtype dtype, const void* x,
+                        const int32_t* topk_idx, const float* topk_w, const void* workspace,
+                        size_t workspace_bytes, int32_t recv_capacity, void* recv_x,
+                        float* recv_scales, int32_t* recv_src_idx, int32_t* recv_topk_idx,
+                        float* recv_topk_w, int32_t* rank_offsets, int32_t* send_row,
+                        int32_t* num_recv, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape s = *shape;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = dtype == MOE_FP8_E4M3;
+  if (fp8 && s.hidden % moe::kFp8Block != 0) return MOE_ERR_INVALID_ARG;
+  if (!x || !topk_idx || !topk_w || !workspace || !recv_x || !recv_src_idx || !recv_topk_idx ||
+      !recv_topk_w || !rank_offsets || !send_row || !num_recv || (fp8 && !recv_scales))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
+      !aligned(workspace, kPlanAlign) || !aligned(recv_src_idx, 4) || !aligned(recv_topk_idx, 4) ||
+      !aligned(recv_topk_w, 4) || !aligned(rank_offsets, 4) || !aligned(send_row, 4) ||
+      !aligned(num_recv, 4) || (fp8 && !aligned(recv_scales, 4)))
+    return MOE_ERR_INVALID_ARG;
+  const PlanLayout p = plan_layout(s);
+  if (workspace_bytes < p.total) return MOE_ERR_INVALID_ARG;
+  if (recv_capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (recv_capacity < s.num_tokens * std::min(s.num_topk, s.num_ranks)) return MOE_ERR_CAPACITY;
+
+  const char* ws = static_cast<const char*>(workspace);
+  moe::DispatchArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.token_ranks = reinterpret_cast<const uint64_t*>(ws + p.token_ranks);
+  a.chunk_base = reinterpret_cast<const int32_t*>(ws + p.chunk_base);
+  a.ws_rank_offsets = reinterpret_cast<const int32_t*>(ws + p.rank_offsets);
+  a.recv_x = recv_x;
+  a.recv_scales = recv_scales;
+  a.recv_src_idx = recv_src_idx;
+  a.recv_topk_idx = recv_topk_idx;
+  a.recv_topk_w = recv_topk_w;
+  a.rank_offsets = rank_offsets;
+  a.send_row = send_row;
+  a.num_recv = num_recv;
+  a.rank_magic = rank_magic(s);
+  a.rank_bits = s.num_ranks == 64 ? ~0ull : ((1ull << s.num_ranks) - 1);
+  a.T = s.num_tokens;
+  a.H = s.hidden;
+  a.H8 = s.hidden / 8;
+  a.k = s.num_topk;
+  a.E = s.num_experts;
+  a.R = s.num_ranks;
+  a.L = s.num_experts / s.num_ranks;
+  a.NC = p.NC;
+  a.capacity = recv_capacity;
+#ifdef MOE_FORCE_DISPATCH_U
+  const int U = MOE_FORCE_DISPATCH_U;
+#else
+  const int U = pick_chunks_per_lane(s.num_tokens, a.H8);
+#endif
+  const int groups = (a.H8 + moe::kWave - 1) / moe::kWave;
+  a.slices = (groups + U - 1) / U;
+  if ((int64_t)s.num_tokens * a.slices > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  a.items = s.num_tokens * a.slices;
+  const int waves_per_block = moe::kDispatchBlock / moe::kWave;
+  const dim3 grid(std::max(1, (a.items + waves_per_block - 1) / waves_per_block));
+  if (fp8)
+    launch_dispatch<true>(U, grid, stream, a);
+  else
+    launch_dispatch<false>(U, grid, stream, a);
+  return last_launch_status();
+}
+
+moe_status moe_combine(const moe_shape* shape, const void* y, int32_t num_y_rows,
+                       const int32_t* topk_idx, const float* topk_w, const int32_t* send_row,
+                       void* out, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape s = *shape;
+  if (num_y_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (!y || !topk_idx || !topk_w || !send_row || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
+      !aligned(send_row, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (s.num_tokens == 0) return MOE_OK;
+
+  moe::CombineArgs a{};
+  a.y = static_cast<const uint16_t*>(y);
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.send_row = send_row;
+  a.out = static_cast<uint16_t*>(out);
+  a.rank_magic = rank_magic(s);
+  a.T = s.num_tokens;
+  a.H = s.hidden;
+  a.H8 = s.hidden / 8;
+  a.k = s.num_topk;
+  a.E = s.num_experts;
+  a.R = s.num_ranks;
+  a.num_y_rows = num_y_rows;
+#ifdef MOE_FORCE_COMBINE_U
+  const int U = MOE_FORCE_COMBINE_U;
+#else
+  const int U = std::min(2, pick_chunks_per_lane(s.num_tokens, a.H8));
+#endif
+  const int groups = (a.H8 + moe::kWave - 1) / moe::kWave;
+  a.slices = (groups + U - 1) / U;
+  if ((int64_t)s.num_tokens * a.slices > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  a.items = s.num_tokens * a.slices;
+  const int waves_per_block = moe::kCombineBlock / moe::kWave;
+  const dim3 grid((a.items + waves_per_block - 1) / waves_per_block);
+  launch_combine(U, grid, stream, a);
+  return last_launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+/*
+ * moe_ep.h — C ABI of the MI355X (gfx950) MoE expert-parallel dispatch/combine library.
+ *
+ * The library computes, on one GPU, the data-parallel core of expert-parallel
+ * MoE communication as DeepEP describes it:
+ *
+ *   1. dispatch layout  — top-k expert ids -> per-rank and per-expert token
+ *                         counts and the is_token_in_rank mask;
+ *   2. dispatch         — each token's hidden row is packed, once per distinct
+ *                         destination rank, into that rank's receive segment
+ *                         (bf16 bit copy, or FP8 E4M3 with one fp32 scale per
+ *                         128 channels);
+ *   3. combine          — expert outputs are gathered back to their source
+ *                         tokens as a top-k weighted fp32 sum, rounded to bf16.
+ *
+ * Passages followed (page titles as printed on the pages):
+ *   [overlap notes]  "DeepEP：年度总结中的计算通信重叠摘记" (notes.kuangjux.top),
+ *                    section 节点内通信 (intranode communication): only ranks
+ *                    owning a selected expert receive a token (the
+ *                    is_token_in_rank matrix), dispatch may carry FP8, and
+ *                    dispatch and combine are the two measured exchange steps.
+ *   [rocSHMEM notes] mlqm.cn notes on rocSHMEM and the RDMA buffer, section 3.2:
+ *                    the exchange buffer holds packed outgoing rows and
+ *                    received rows, is reused by combine, is allocated once
+ *                    and sized for the worst case.
+ *   [DeepEP overview] "DeepEP：面向MoE的高吞吐低延迟GPU通信库" (ssnai.com):
+ *                    dispatch/combine kernels with FP8 and stream-ordered use.
+ *
+ * Logical ranks: the R destination ranks are R contiguous segments of one
+ * receive buffer in this GPU's memory (rank r's rows are
+ * [rank_offsets[r], rank_offsets[r+1])).  Expert e lives on rank e / L,
+ * L = E / R.  Expert ids outside [0, E) are masked: every step skips them.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All array pointers are DEVICE pointers owned by the caller; the library
+ *   allocates nothing and keeps no state between calls.  Outputs must not
+ *   alias inputs.  `shape` is a HOST pointer, read during the call only.
+ * - Layout is row-major and densely packed.  bf16 values are passed as raw
+ *   16-bit patterns.  Payload pointers (x, recv_x, y, out) must be 16-byte
+ *   aligned; int32/float arrays 4-byte aligned.
+ * - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *   without waiting; nothing is read back to the host.
+ * - Arguments are checked on the host before anything is enqueued; on any
+ *   error nothing is launched and no memory is touched.  A launch failure
+ *   reported by the runtime returns MOE_ERR_HIP.
+ * - Limits: 0 <= T, 1 <= k <= 32, 1 <= R <= 64, R <= E <= 4096, E % R == 0,
+ *   H > 0 and H % 8 == 0 (H % 128 == 0 for FP8), T*k and T*R below 2^31.
+ */
+#ifndef MOE_EP_H_
+#define MOE_EP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_shape {
+  int32_t num_tokens;  /* T: tokens of this source batch */
+  int32_t hidden;      /* H: channels per token row */
+  int32_t num_topk;    /* k: expert slots per token */
+  int32_t num_experts; /* E */
+  int32_t num_ranks;   /* R: logical destination ranks */
+} moe_shape;
+
+typedef enum moe_dtype {
+  MOE_BF16 = 0,     /* receive rows are bf16 bit copies of x */
+  MOE_FP8_E4M3 = 1  /* receive rows are OCP E4M3 bytes + fp32 scale per 128 channels */
+} moe_dtype;
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad shape, workspace too small */
+  MOE_ERR_CAPACITY = 2,    /* receive capacity below T * min(k, R) */
+  MOE_ERR_UNSUPPORTED = 3, /* shape outside the limits above */
+  MOE_ERR_HIP = 4          /* the HIP runtime reported a launch error */
+} moe_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(moe_status status);
+
+/* Bytes of device workspace the layout writes and dispatch reads for `shape`
+ * (0 if the shape is invalid).  The workspace is the dispatch plan: the
+ * per-token rank bitmasks, per-64-token-chunk prefix counts per rank and the
+ * rank offsets.  It carries no state across different layouts. */
+size_t moe_workspace_bytes(const moe_shape* shape);
+
+/* Worst-case receive rows, T * min(k, R): every token sent to min(k, R)
+ * distinct ranks.  [rocSHMEM notes 3.2: the buffer is sized once for the worst
+ * case.]  Returns -1 if the shape is invalid. */
+int32_t moe_max_recv_rows(const moe_shape* shape);
+
+/* Dispatch layout.  [overlap notes, 节点内通信: the is_token_in_rank filter.]
+ *
+ *   topk_idx          in  int32[T, k]   expert id per slot (ids outside [0,E) masked)
+ *   tokens_per_rank   out int32[R]      number of tokens sent to each rank
+ *   tokens_per_expert out int32[E]      number of valid slots naming each expert
+ *   is_token_in_rank  out uint8[T, R]   1 iff a valid slot of token t names an expert of rank r, else 0
+ *   workspace         out bytes[ws]     dispatch plan consumed by moe_dispatch
+ *                                       (workspace_bytes >= moe_workspace_bytes(shape))
+ */
+moe_status moe_get_dispatch_layout(const moe_shape* shape, const int32_t* topk_idx,
+                                   int32_t* tokens_per_rank, int32_t* tokens_per_expert,
+                                   uint8_t* is_token_in_rank, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/* Dispatch.  [overlap notes, 节点内通信: filtered send, FP8 transport;
+ * rocSHMEM notes 3.2: rows packed into a preallocated receive buffer.]
+ *
+ * Receive row of (token t, rank r) = rank_offsets[r] + number of tokens t' < t
+ * that also go to r: segments in rank order, rows in ascending token order.
+ *
+ *   dtype          MOE_BF16 or MOE_FP8_E4M3
+ *   x              in  bf16[T, H]
+ *   topk_idx       in  int32[T, k]     the ids the layout was computed from
+ *   topk_w         in  float[T, k]     gate weights
+ *   workspace      in  bytes[ws]       written by moe_get_dispatch_layout for the same topk_idx
+ *   recv_capacity      rows allocated in the receive arrays; >= T * min(k, R)
+ *   recv_x         out bf16[cap, H] (MOE_BF16) or uint8[cap, H] (MOE_FP8_E4M3)
+ *   recv_scales    out float[cap, H/128]  dequantisation scale s per 128-channel
+ *                      block (x ~= decode(q) * s), s = fl32(max(amax, 1e-4) / 448),
+ *                      q = E4M3_RNE(fl32(x / s)); NULL allowed (and ignored) for MOE_BF16
+ *   recv_src_idx   out int32[cap]      source token of each receive row
+ *   recv_topk_idx  out int32[cap, k]   local expert id (e - r*L) of slot j if it
+ *                                      names an expert of the row's rank, else -1
+ *   recv_topk_w    out float[cap, k]   weight of slot j where recv_topk_idx >= 0, else +0.0
+ *   rank_offsets   out int32[R + 1]    segment starts; rank_offsets[R] = number of rows
+ *   send_row       out int32[T, R]     receive row of (t, r), or -1 if t is not sent to r
+ *   num_recv       out int32[1]        number of receive rows written (= rank_offsets[R])
+ *
+ * Rows at or beyond num_recv are not written.
+ */
+moe_status moe_dispatch(const moe_shape* shape, moe_dtype dtype, const void* x,
+                        const int32_t* topk_idx, const float* topk_w, const void* workspace,
+                        size_t workspace_bytes, int32_t recv_capacity, void* recv_x,
+                        float* recv_scales, int32_t* recv_src_idx, int32_t* recv_topk_idx,
+                        float* recv_topk_w, int32_t* rank_offsets, int32_t* send_row,
+                        int32_t* num_recv, hipStream_t stream);
+
+/* Combine.  [overlap notes, 节点内通信: combine; rocSHMEM notes 3.2: the
+ * receive buffer is reused for the returning expert outputs.]
+ *
+ * out[t, c] = BF16_RNE(acc) with acc = +0 and, for j = 0..k-1 in order over
+ * valid slots, acc = fl32(acc + fl32(topk_w[t, j] * y[send_row[t, e_tj / L], c]))
+ * (no fused multiply-add).  Tokens without a valid slot get +0.
+ *
+ *   y          in  bf16[num_y_rows, H]  expert outputs in receive-row order
+ *   num_y_rows     rows of y; slots whose row is outside [0, num_y_rows) are skipped
+ *   topk_idx   in  int32[T, k]
+ *   topk_w     in  float[T, k]
+ *   send_row   in  int32[T, R]          from moe_dispatch
+ *   out        out bf16[T, H]
+ */
+moe_status moe_combine(const moe_shape* shape, const void* y, int32_t num_y_rows,
+                       const int32_t* topk_idx, const float* topk_w, const int32_t* send_row,
+                       void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H_ */

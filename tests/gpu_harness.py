@@ -1,0 +1,78 @@
+"""Runs the HIP path through the C ABI on seeded inputs and returns numpy results.
+
+Used by the GPU parity tests, the smoke check and nothing else.  Output
+buffers are pre-filled with a poison byte so that tests can check which rows
+were written; receive buffers get extra guard rows after the capacity.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+import combine_get_dispatch_07_amd as moe
+
+POISON = 0x7B
+GUARD_ROWS = 3
+
+
+def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bf16_to_np(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _poison(d: Dict[str, Optional[torch.Tensor]]) -> None:
+    for v in d.values():
+        if v is not None:
+            v.view(torch.uint8).fill_(POISON)
+
+
+class PathResult(dict):
+    pass
+
+
+def run_layout_dispatch(x: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, E: int, R: int, dtype: str,
+                        guard: int = GUARD_ROWS) -> PathResult:
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    shape = moe.MoeShape(T, H, k, E, R)
+    xd = to_dev_bf16(x) if T else torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    idx_d = torch.from_numpy(np.ascontiguousarray(topk_idx, dtype=np.int32)).cuda()
+    w_d = torch.from_numpy(np.ascontiguousarray(topk_w, dtype=np.float32)).cuda()
+    lay = moe.alloc_layout(shape)
+    _poison(lay)
+    moe.run_layout(shape, idx_d, lay)
+    cap = moe.max_recv_rows(shape)
+    d = moe.alloc_dispatch(shape, dtype, capacity=cap + guard)
+    _poison(d)
+    moe.run_dispatch(shape, dtype, xd, idx_d, w_d, lay, d)
+    torch.cuda.synchronize()
+    r = PathResult()
+    r["shape"] = shape
+    r["cap"] = cap
+    r["tokens_per_rank"] = lay["tokens_per_rank"].cpu().numpy()
+    r["tokens_per_expert"] = lay["tokens_per_expert"].cpu().numpy()
+    r["is_token_in_rank"] = lay["is_token_in_rank"].cpu().numpy()
+    for key in ("recv_src_idx", "recv_topk_idx", "recv_topk_w", "rank_offsets", "send_row", "num_recv"):
+        r[key] = d[key].cpu().numpy()
+    if dtype == "bf16":
+        r["recv_x"] = bf16_to_np(d["recv_x"])
+    else:
+        r["recv_x"] = d["recv_x"].cpu().numpy()
+        r["recv_scales"] = d["recv_scales"].cpu().numpy()
+    r["_dev"] = {"x": xd, "idx": idx_d, "w": w_d, "lay": lay, "d": d}
+    return r
+
+
+def run_combine(shape, y: np.ndarray, idx_d: torch.Tensor, w_d: torch.Tensor, send_row_d: torch.Tensor,
+                num_y_rows: Optional[int] = None) -> np.ndarray:
+    yd = to_dev_bf16(y) if y.shape[0] else torch.empty((0, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((shape.num_tokens, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    out.view(torch.uint8).fill_(POISON)
+    moe.moe_combine(shape, yd, idx_d, w_d, send_row_d, out, num_y_rows=num_y_rows)
+    torch.cuda.synchronize()
+    return bf16_to_np(out)

@@ -1,0 +1,328 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: layout, slots, metadata, bf16 rows, FP8 bytes and scales bit-exact;
+combine within 1 bf16 ulp (and, since both sides sum in the same fp32 order
+without fused multiply-add, expected bit-exact).  Receive buffers carry poison
+and guard rows: rows at or beyond num_recv must stay untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import moe_oracle as O
+from oracle.numerics import E4M3_MAGNITUDES, bf16_bits_to_f32, f32_to_bf16_bits_rne
+from tests.checks import (check_combine_bound, check_fp8_block_properties, check_layout_invariants,
+                          check_slot_invariants, within_one_bf16_ulp)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests import gpu_harness  # noqa: F401  (loads the HIP library; fails loudly if missing)
+
+
+def H():
+    from tests import gpu_harness
+    return gpu_harness
+
+
+def _print_case(name, **kw):
+    print(f"[case] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def check_layout_and_slots(res, idx, E, R):
+    tpr, tpe, mask = O.get_dispatch_layout(idx, E, R)
+    assert np.array_equal(res["tokens_per_expert"], tpe)
+    assert np.array_equal(res["tokens_per_rank"], tpr)
+    assert np.array_equal(res["is_token_in_rank"], mask)
+    offs, send_row, n = O.assign_slots(mask)
+    assert np.array_equal(res["rank_offsets"], offs)
+    assert int(res["num_recv"][0]) == n
+    assert np.array_equal(res["send_row"], send_row)
+    return send_row, n
+
+
+def check_metadata_and_guards(res, idx, w, E, R, send_row, n):
+    src, ridx, rw = O.dispatch_metadata(idx, w, E, R, send_row, n)
+    assert np.array_equal(res["recv_src_idx"][:n], src)
+    assert np.array_equal(res["recv_topk_idx"][:n], ridx)
+    assert np.array_equal(res["recv_topk_w"][:n].view(np.uint32), rw.view(np.uint32))
+    poison32 = np.uint32(0x7B7B7B7B)
+    for key in ("recv_src_idx", "recv_topk_idx", "recv_topk_w"):
+        tail = res[key][n:].view(np.uint32)
+        assert (tail == poison32).all(), f"{key} written beyond num_recv"
+    tail = res["recv_x"][n:].view(np.uint8)
+    assert (tail == 0x7B).all(), "recv_x written beyond num_recv"
+    if "recv_scales" in res:
+        assert (res["recv_scales"][n:].view(np.uint32) == poison32).all()
+    return src
+
+
+def check_payload(res, x, src, n, dtype, sample_tokens=None):
+    if dtype == "bf16":
+        if sample_tokens is None:
+            assert np.array_equal(res["recv_x"][:n], O.dispatch_rows_bf16(x, src))
+        else:
+            rows = np.nonzero(np.isin(src, sample_tokens))[0]
+            assert np.array_equal(res["recv_x"][rows], O.dispatch_rows_bf16(x, src[rows]))
+        return
+    toks = np.arange(x.shape[0]) if sample_tokens is None else np.asarray(sample_tokens)
+    q_tok, s_tok = O.quantize_fp8_blocks(x[toks])
+    pos = np.full(x.shape[0], -1, dtype=np.int64)
+    pos[toks] = np.arange(toks.size)
+    rows = np.nonzero(pos[src] >= 0)[0]
+    got_q = res["recv_x"][rows]
+    got_s = res["recv_scales"][rows]
+    exp_q = q_tok[pos[src[rows]]]
+    exp_s = s_tok[pos[src[rows]]]
+    bad = np.nonzero((got_q != exp_q).any(axis=1))[0]
+    assert bad.size == 0, f"fp8 bytes differ in {bad.size} rows, first row {rows[bad[0]]}"
+    assert np.array_equal(got_s.view(np.uint32), exp_s.view(np.uint32))
+
+
+def check_combine(res, y, idx, w, E, R, send_row, tokens=None, num_y_rows=None):
+    dev = res["_dev"]
+    out = H().run_combine(res["shape"], y, dev["idx"], dev["w"], dev["d"]["send_row"], num_y_rows=num_y_rows)
+    toks = np.arange(idx.shape[0]) if tokens is None else np.asarray(tokens)
+    ref = O.combine(y, idx, w, send_row, E, R, tokens=toks)
+    got = out[toks]
+    ok = within_one_bf16_ulp(got, ref)
+    assert ok.all(), f"{(~ok).sum()} combine outputs beyond 1 bf16 ulp"
+    exact = np.array_equal(got, ref)
+    ref64, mag = O.combine_f64(y, idx, w, send_row, E, R, tokens=toks)
+    check_combine_bound(got, ref64, mag, idx.shape[1])
+    return out, exact
+
+
+def run_case(x, idx, w, E, R, dtype, y=None, sample_tokens=None, combine_tokens=None, identity=False):
+    res = H().run_layout_dispatch(x, idx, w, E, R, dtype)
+    send_row, n = check_layout_and_slots(res, idx, E, R)
+    src = check_metadata_and_guards(res, idx, w, E, R, send_row, n)
+    check_payload(res, x, src, n, dtype, sample_tokens)
+    exact = None
+    if identity:
+        if dtype == "bf16":
+            y = res["recv_x"][:n]
+        else:
+            y = O.dequantize_fp8_to_bf16(res["recv_x"][:n], res["recv_scales"][:n])
+    if y is not None:
+        _, exact = check_combine(res, y, idx, w, E, R, send_row, tokens=combine_tokens)
+    return res, exact
+
+
+# ------------------------------------------------------------------ the five workloads
+
+@pytest.mark.parametrize("cfg", W.CONFIGS, ids=lambda c: c.name)
+def test_workload_parity(cfg):
+    _print_case("workload", name=cfg.name, T=cfg.num_tokens, H=cfg.hidden, E=cfg.num_experts,
+                k=cfg.num_topk, R=cfg.num_ranks, dtype=cfg.dispatch_dtype)
+    d = W.make_inputs(cfg)
+    x, idx, w = d["x"], d["topk_idx"], d["topk_w"]
+    E, R, T = cfg.num_experts, cfg.num_ranks, cfg.num_tokens
+    big = T * cfg.hidden > 8_000_000
+    rng = np.random.default_rng(cfg.index)
+    sample = np.sort(rng.choice(T, size=min(T, 384), replace=False)) if big else None
+    y = None
+    if cfg.combine_input == "random":
+        _, _, mask = O.get_dispatch_layout(idx, E, R)
+        n = int(mask.sum())
+        y = W.draw_expert_outputs(W.y_stream(cfg), n, cfg.hidden)
+    _, exact = run_case(x, idx, w, E, R, cfg.dispatch_dtype, y=y, sample_tokens=sample, combine_tokens=sample,
+                        identity=cfg.combine_input == "identity")
+    assert exact, "combine not bit-identical to the fp32-sequenced oracle"
+
+
+# ------------------------------------------------------------------ edge cases
+
+EDGE = [
+    # name, seed, T, H, E, k, R, dtype, invalid_frac
+    ("single_token", 1, 1, 256, 16, 4, 4, "bf16", 0.0),
+    ("ragged_multiblock", 2, 4097, 512, 64, 6, 16, "bf16", 0.1),
+    ("fused_limit", 3, 1024, 256, 32, 4, 8, "fp8", 0.05),
+    ("first_multiblock", 4, 1025, 256, 32, 4, 8, "fp8", 0.05),
+    ("one_rank", 5, 300, 256, 8, 2, 1, "bf16", 0.0),
+    ("top1", 6, 777, 384, 64, 1, 8, "fp8", 0.0),
+    ("max_limits", 7, 300, 128, 4096, 32, 64, "fp8", 0.1),
+    ("mostly_invalid", 8, 500, 256, 16, 4, 4, "bf16", 0.6),
+    ("ragged_slice_fp8", 9, 200, 640, 32, 4, 8, "fp8", 0.0),
+    ("ragged_slice_bf16", 10, 200, 136, 32, 4, 8, "bf16", 0.0),
+    ("R_not_multiple_of_4", 11, 333, 256, 30, 5, 6, "bf16", 0.1),
+    ("R_64_k_8", 12, 2000, 256, 256, 8, 64, "bf16", 0.0),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: c[0])
+def test_edge_parity(case):
+    name, seed, T, Hd, E, k, R, dtype, inv = case
+    _print_case("edge", name=name, T=T, H=Hd, E=E, k=k, R=R, dtype=dtype)
+    d = W.random_case(seed, T, Hd, E, k, R, invalid_frac=inv)
+    _, _, mask = O.get_dispatch_layout(d["topk_idx"], E, R)
+    y = W.draw_expert_outputs(np.random.default_rng(seed), max(int(mask.sum()), 1), Hd)
+    _, exact = run_case(d["x"], d["topk_idx"], d["topk_w"], E, R, dtype, y=y)
+    assert exact
+
+
+def test_empty_batch():
+    _print_case("edge", name="empty")
+    x = np.zeros((0, 256), np.uint16)
+    idx = np.zeros((0, 4), np.int32)
+    w = np.zeros((0, 4), np.float32)
+    res = H().run_layout_dispatch(x, idx, w, 16, 4, "bf16")
+    assert (res["tokens_per_rank"] == 0).all() and (res["tokens_per_expert"] == 0).all()
+    assert (res["rank_offsets"] == 0).all() and int(res["num_recv"][0]) == 0
+    assert (res["recv_x"].view(np.uint8) == 0x7B).all()
+    out = H().run_combine(res["shape"], np.zeros((0, 256), np.uint16), res["_dev"]["idx"], res["_dev"]["w"],
+                          res["_dev"]["d"]["send_row"])
+    assert out.shape == (0, 256)
+
+
+def test_all_tokens_to_one_rank():
+    _print_case("edge", name="hot_rank")
+    rng = np.random.default_rng(21)
+    T, Hd, E, k, R = 3000, 256, 64, 4, 8
+    L = E // R
+    idx = np.stack([rng.permutation(L)[:k] + 3 * L for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    x = W.draw_hidden(rng, T, Hd)
+    y = W.draw_expert_outputs(rng, T, Hd)
+    res, exact = run_case(x, idx, w, E, R, "fp8", y=y)
+    assert res["tokens_per_rank"].tolist() == [0, 0, 0, T, 0, 0, 0, 0]
+    assert exact
+
+
+def test_duplicate_ids_in_a_row():
+    _print_case("edge", name="duplicates")
+    rng = np.random.default_rng(22)
+    T, Hd, E, k, R = 200, 256, 16, 4, 4
+    idx = rng.integers(0, 6, size=(T, k)).astype(np.int32)  # many repeats
+    w = rng.random((T, k)).astype(np.float32)
+    x = W.draw_hidden(rng, T, Hd)
+    _, _, mask = O.get_dispatch_layout(idx, E, R)
+    y = W.draw_expert_outputs(rng, int(mask.sum()), Hd)
+    _, exact = run_case(x, idx, w, E, R, "bf16", y=y)
+    assert exact
+
+
+def test_fp8_special_rows():
+    _print_case("edge", name="fp8_special_rows")
+    rng = np.random.default_rng(23)
+    Hd = 512
+    rows = [np.zeros(Hd, np.float32), np.full(Hd, -0.0, np.float32),
+            (rng.standard_normal(Hd) * 1e-6).astype(np.float32),           # amax below the 1e-4 floor
+            np.where(rng.random(Hd) < 0.5, 2.0 ** -130, -3 * 2.0 ** -133).astype(np.float32),  # bf16 subnormals
+            (rng.standard_normal(Hd) * 3e4).astype(np.float32),
+            (rng.standard_normal(Hd) * 1e-30).astype(np.float32)]
+    # E4M3 ties: a block with amax 448 * 2^-3 so that x / s = 8 x exactly hits midpoints
+    tie = np.zeros(Hd, np.float32)
+    tie[0] = 56.0
+    mids = ((E4M3_MAGNITUDES[1:] + E4M3_MAGNITUDES[:-1]) / 2) / 8
+    tie[1:128] = rng.choice(mids[mids <= 56], 127) * rng.choice([-1, 1], 127)
+    rows.append(tie)
+    x = f32_to_bf16_bits_rne(np.stack(rows))
+    T = x.shape[0]
+    idx = np.tile(np.array([[0, 5]], np.int32), (T, 1))
+    w = np.full((T, 2), 0.5, np.float32)
+    res, _ = run_case(x, idx, w, 8, 2, "fp8")
+    n = int(res["num_recv"][0])
+    check_fp8_block_properties(x[res["recv_src_idx"][:n]], res["recv_x"][:n], res["recv_scales"][:n])
+
+
+def test_fp8_sweep_all_bf16_patterns():
+    """Every finite bf16 value, quantised against power-of-two scales (exact ties) and random scales."""
+    _print_case("edge", name="fp8_sweep")
+    rng = np.random.default_rng(24)
+    allb = np.arange(2 ** 16, dtype=np.uint32).astype(np.uint16)
+    fin = allb[np.isfinite(bf16_bits_to_f32(allb))]
+    Hd = 7168
+    blocks = []
+    amaxes = [448.0 * 2.0 ** e for e in range(-20, 8)] + list(np.exp2(rng.uniform(-15, 10, 40)))
+    for a in amaxes:
+        a_bits = f32_to_bf16_bits_rne(np.float32([a]))[0]
+        af = bf16_bits_to_f32(np.uint16([a_bits]))[0]
+        vals = fin[np.abs(bf16_bits_to_f32(fin)) <= af]
+        vals = rng.permutation(vals)
+        for b0 in range(0, vals.size, 127):
+            blk = np.zeros(128, np.uint16)
+            chunk = vals[b0:b0 + 127]
+            blk[0] = a_bits
+            blk[1:1 + chunk.size] = chunk
+            blocks.append(blk)
+    nb = len(blocks)
+    per_row = Hd // 128
+    pad = (-nb) % per_row
+    blocks += [np.zeros(128, np.uint16)] * pad
+    x = np.stack(blocks).reshape(-1, Hd)
+    T = x.shape[0]
+    idx = np.tile(np.array([[0]], np.int32), (T, 1))
+    w = np.ones((T, 1), np.float32)
+    print(f"[case] fp8 sweep rows={T} blocks={nb}", flush=True)
+    run_case(x, idx, w, 8, 8, "fp8")
+
+
+# ------------------------------------------------------------------ combine-specific
+
+def test_combine_skips_rows_beyond_num_y_rows():
+    _print_case("edge", name="num_y_rows")
+    d = W.random_case(31, 300, 256, 32, 4, 8)
+    x, idx, w = d["x"], d["topk_idx"], d["topk_w"]
+    res = H().run_layout_dispatch(x, idx, w, 32, 8, "bf16")
+    send_row, n = check_layout_and_slots(res, idx, 32, 8)
+    y = W.draw_expert_outputs(np.random.default_rng(1), n, 256)
+    limit = n // 2
+    dev = res["_dev"]
+    out = H().run_combine(res["shape"], y[:limit], dev["idx"], dev["w"], dev["d"]["send_row"], num_y_rows=limit)
+    L = 32 // 8
+    rows = np.take_along_axis(send_row, np.where(idx >= 0, idx // L, 0), axis=1)
+    idx_cut = np.where(rows < limit, idx, -1).astype(np.int32)
+    ref = O.combine(y[:limit], idx_cut, w, send_row, 32, 8)
+    assert np.array_equal(out, ref)
+
+
+def test_bf16_round_trip_identity_expert():
+    """Dispatch then identity-expert combine returns sum_j w_j x = x for normalised weights."""
+    cfg = W.CONFIG_BY_NAME["prefill"]
+    c = W.with_tokens(cfg, 512)
+    _print_case("roundtrip", T=c.num_tokens)
+    d = W.make_inputs(c)
+    x, idx, w = d["x"], d["topk_idx"], d["topk_w"]
+    res, exact = run_case(x, idx, w, c.num_experts, c.num_ranks, "bf16", identity=True)
+    assert exact
+    n = int(res["num_recv"][0])
+    dev = res["_dev"]
+    out = H().run_combine(res["shape"], res["recv_x"][:n], dev["idx"], dev["w"], dev["d"]["send_row"])
+    xf = bf16_bits_to_f32(x).astype(np.float64) * w.astype(np.float64).sum(axis=1, keepdims=True)
+    check_combine_bound(out, xf, np.abs(xf), c.num_topk)
+    assert within_one_bf16_ulp(out, x).all()
+
+
+def test_run_to_run_identical():
+    cfg = W.CONFIG_BY_NAME["group_limited"]
+    c = W.with_tokens(cfg, 1500)
+    _print_case("determinism", T=c.num_tokens)
+    d = W.make_inputs(c)
+    a = H().run_layout_dispatch(d["x"], d["topk_idx"], d["topk_w"], c.num_experts, c.num_ranks, "fp8")
+    b = H().run_layout_dispatch(d["x"], d["topk_idx"], d["topk_w"], c.num_experts, c.num_ranks, "fp8")
+    for key in ("tokens_per_rank", "tokens_per_expert", "is_token_in_rank", "send_row", "recv_x", "recv_scales",
+                "recv_src_idx", "recv_topk_idx", "recv_topk_w"):
+        assert np.array_equal(a[key], b[key]), key
+    n = int(a["num_recv"][0])
+    y = W.draw_expert_outputs(np.random.default_rng(3), n, c.hidden)
+    o1 = H().run_combine(a["shape"], y, a["_dev"]["idx"], a["_dev"]["w"], a["_dev"]["d"]["send_row"])
+    o2 = H().run_combine(a["shape"], y, a["_dev"]["idx"], a["_dev"]["w"], a["_dev"]["d"]["send_row"])
+    assert np.array_equal(o1, o2)
+
+
+def test_layout_invariants_at_full_size():
+    cfg = W.CONFIG_BY_NAME["skewed"]
+    _print_case("invariants", name=cfg.name)
+    g = W.seed_streams(cfg.index)
+    idx, w = W.route(cfg, g[1], g[3])
+    x = np.zeros((cfg.num_tokens, 128), np.uint16)
+    res = H().run_layout_dispatch(x, idx, w, cfg.num_experts, cfg.num_ranks, "bf16")
+    check_layout_invariants(idx, cfg.num_experts, cfg.num_ranks, res["tokens_per_rank"], res["tokens_per_expert"],
+                            res["is_token_in_rank"])
+    check_slot_invariants(res["is_token_in_rank"], res["rank_offsets"], res["send_row"], int(res["num_recv"][0]))
