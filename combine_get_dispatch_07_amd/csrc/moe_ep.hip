@@ -69,6 +69,9 @@ uint64_t rank_magic(const moe_shape& s) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// A pointer may be NULL exactly when the array it stands for is empty.
+bool present(const void* p, int64_t elements) { return p != nullptr || elements == 0; }
+
 // Chunks of 8 channels per lane per work item, from the instantiated set.
 // Fewer, wider items amortise the per-item slot arithmetic; narrower ones
 // give small batches enough waves to fill the chip.
@@ -140,7 +143,9 @@ moe_status moe_get_dispatch_layout(const moe_shape* shape, const int32_t* topk_i
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape s = *shape;
-  if (!topk_idx || !tokens_per_rank || !tokens_per_expert || !is_token_in_rank || !workspace)
+  const int64_t T = s.num_tokens;
+  if (!present(topk_idx, T) || !present(is_token_in_rank, T) || !tokens_per_rank || !tokens_per_expert ||
+      !workspace)
     return MOE_ERR_INVALID_ARG;
   if (!aligned(topk_idx, 4) || !aligned(tokens_per_rank, 4) || !aligned(tokens_per_expert, 4) ||
       !aligned(workspace, kPlanAlign))
@@ -191,8 +196,10 @@ moe_status moe_dispatch(const moe_shape* shape, moe_dtype dtype, const void* x,
   if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   const bool fp8 = dtype == MOE_FP8_E4M3;
   if (fp8 && s.hidden % moe::kFp8Block != 0) return MOE_ERR_INVALID_ARG;
-  if (!x || !topk_idx || !topk_w || !workspace || !recv_x || !recv_src_idx || !recv_topk_idx ||
-      !recv_topk_w || !rank_offsets || !send_row || !num_recv || (fp8 && !recv_scales))
+  const int64_t T = s.num_tokens, cap = recv_capacity;
+  if (!present(x, T) || !present(topk_idx, T) || !present(topk_w, T) || !present(send_row, T) || !workspace ||
+      !present(recv_x, cap) || !present(recv_src_idx, cap) || !present(recv_topk_idx, cap) ||
+      !present(recv_topk_w, cap) || (fp8 && !present(recv_scales, cap)) || !rank_offsets || !num_recv)
     return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
       !aligned(workspace, kPlanAlign) || !aligned(recv_src_idx, 4) || !aligned(recv_topk_idx, 4) ||
@@ -256,7 +263,10 @@ moe_status moe_combine(const moe_shape* shape, const void* y, int32_t num_y_rows
   if (st != MOE_OK) return st;
   const moe_shape s = *shape;
   if (num_y_rows < 0) return MOE_ERR_INVALID_ARG;
-  if (!y || !topk_idx || !topk_w || !send_row || !out) return MOE_ERR_INVALID_ARG;
+  const int64_t T = s.num_tokens;
+  if (!present(y, num_y_rows) || !present(topk_idx, T) || !present(topk_w, T) || !present(send_row, T) ||
+      !present(out, T))
+    return MOE_ERR_INVALID_ARG;
   if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
       !aligned(send_row, 4))
     return MOE_ERR_INVALID_ARG;

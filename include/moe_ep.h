@@ -35,7 +35,9 @@
  * ---------------------------------
  * - All array pointers are DEVICE pointers owned by the caller; the library
  *   allocates nothing and keeps no state between calls.  Outputs must not
- *   alias inputs.  `shape` is a HOST pointer, read during the call only.
+ *   alias inputs.  An array pointer may be NULL exactly when the array has
+ *   no elements (T == 0, capacity 0, no rows of y).  `shape` is a HOST
+ *   pointer, read during the call only.
  * - Layout is row-major and densely packed.  bf16 values are passed as raw
  *   16-bit patterns.  Payload pointers (x, recv_x, y, out) must be 16-byte
  *   aligned; int32/float arrays 4-byte aligned.

@@ -49,8 +49,8 @@ def dispatch(s, dtype=0, cap=None, x=A, scales=A, ws=A, ws_bytes=1 << 30, recv_x
                               p["src"], p["ridx"], p["rw"], p["offs"], p["send"], p["n"], None)
 
 
-def combine(s, y=A, rows=10, out=A):
-    return L.lib.moe_combine(ctypes.byref(s), y, rows, A, A, A, out, None)
+def combine(s, y=A, rows=10, out=A, topk=A, w=A, send=A):
+    return L.lib.moe_combine(ctypes.byref(s), y, rows, topk, w, send, out, None)
 
 
 def test_status_strings():
@@ -120,6 +120,9 @@ def test_combine_errors_and_empty():
     assert combine(s, y=A + 2) == INVALID
     assert combine(s, out=A + 4) == INVALID
     assert combine(shape(T=0)) == OK  # nothing to launch
+    # empty arrays may be NULL (torch gives zero-size tensors a null pointer)
+    assert combine(shape(T=0), y=None, rows=0, out=None, topk=None, w=None, send=None) == OK
+    assert combine(shape(T=5), out=None) == INVALID  # five tokens need an output array
 
 
 def test_binding_rejects_host_tensors():

@@ -30,8 +30,8 @@ def H():
     return gpu_harness
 
 
-def _print_case(name, **kw):
-    print(f"[case] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+def _print_case(label, **kw):
+    print(f"[case] {label} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
 
 
 def check_layout_and_slots(res, idx, E, R):
