@@ -4,8 +4,15 @@
 One step = one pass of the whole path over one batch: dispatch layout ->
 dispatch -> combine (expert outputs are a resident bf16 N(0,1) buffer in
 receive-row order).  Inputs are seeded, synthetic and resident in HBM before
-the timed region.  Per-op times come from HIP events recorded on the stream
-the library launches on; ``value`` is whole-step algorithmic bytes / step time.
+the timed region.  Several independent buffer sets (identical inputs) are
+used in rotation, sized so that one set's data has left the 256 MB
+last-level cache before it is used again.
+
+Timed region: K steps of eager launches on the current stream, with HIP events
+between the ops (per-op times) and a barrier + synchronize on both sides
+(ms_per_step).  ``value`` = whole-step algorithmic bytes / step time.
+After it, each op is also timed as a HIP graph of back-to-back launches
+(``us_kernel``), which removes host launch gaps (they dominate at decode sizes).
 
     python bench.py [--steps K] [--warmup W] [--workload prefill|decode|...]
 
@@ -31,6 +38,8 @@ sys.path.insert(0, ROOT)
 METRIC = "dispatch/combine achieved HBM GB/s + µs/call, 128-tok decode & 4096-tok prefill"
 HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+ROTATION_BYTES = 1 << 30  # buffer sets in rotation cover at least this much memory
+OPS = ("layout", "dispatch", "combine")
 
 
 def log(msg: str) -> None:
@@ -70,71 +79,116 @@ def measured_traffic(workload: str, op: str):
 
 
 class Workload:
-    """Device buffers for one configuration, allocated once (worst-case receive capacity)."""
+    """Device buffers for one configuration: `nsets` rotating sets, each allocated once."""
 
-    def __init__(self, cfg, torch, moe, W):
+    def __init__(self, cfg, torch, moe, W, nsets=None):
         import numpy as np
 
-        self.cfg = cfg
-        self.torch = torch
-        self.moe = moe
+        self.cfg, self.torch, self.moe = cfg, torch, moe
         d = W.make_inputs(cfg)
         self.shape = moe.MoeShape(cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks)
-        self.x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).cuda()
-        self.idx = torch.from_numpy(d["topk_idx"]).cuda()
-        self.w = torch.from_numpy(d["topk_w"]).cuda()
-        self.host = d
-        self.lay = moe.alloc_layout(self.shape)
-        self.disp = moe.alloc_dispatch(self.shape, cfg.dispatch_dtype)
-        self.out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+        x16 = torch.from_numpy(d["x"].view(np.int16))
+        first = self._new_set(x16, d)
         # one pass to learn the receive row count, then expert outputs ~ N(0,1) in receive-row order
-        self.layout()
-        self.dispatch()
+        moe.run_layout(self.shape, first["idx"], first["lay"])
+        moe.run_dispatch(self.shape, cfg.dispatch_dtype, first["x"], first["idx"], first["w"], first["lay"],
+                         first["disp"])
         torch.cuda.synchronize()
-        self.n_recv = int(self.disp["num_recv"].item())
-        y = W.draw_expert_outputs(W.y_stream(cfg), self.n_recv, cfg.hidden)
-        self.y = torch.from_numpy(y.view(np.int16)).view(torch.bfloat16).cuda()
+        self.n_recv = int(first["disp"]["num_recv"].item())
+        y16 = torch.from_numpy(W.draw_expert_outputs(W.y_stream(cfg), self.n_recv, cfg.hidden).view(np.int16))
+        first["y"] = y16.cuda().view(torch.bfloat16)
         self.bytes = algorithmic_bytes(cfg, self.n_recv)
+        footprint = sum(t.numel() * t.element_size() for t in self._tensors(first))
+        if nsets is None:
+            nsets = max(2, min(16, -(-ROTATION_BYTES // footprint)))
+        self.sets = [first]
+        for _ in range(nsets - 1):
+            s = self._new_set(x16, d)
+            s["y"] = y16.cuda().view(torch.bfloat16)
+            self.sets.append(s)
+        self.footprint = footprint
 
-    def layout(self):
-        self.moe.run_layout(self.shape, self.idx, self.lay)
+    def _new_set(self, x16, d):
+        torch, moe, cfg = self.torch, self.moe, self.cfg
+        return {
+            "x": x16.cuda().view(torch.bfloat16),
+            "idx": torch.from_numpy(d["topk_idx"]).cuda(),
+            "w": torch.from_numpy(d["topk_w"]).cuda(),
+            "lay": moe.alloc_layout(self.shape),
+            "disp": moe.alloc_dispatch(self.shape, cfg.dispatch_dtype),
+            "out": torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda"),
+        }
 
-    def dispatch(self):
-        self.moe.run_dispatch(self.shape, self.cfg.dispatch_dtype, self.x, self.idx, self.w, self.lay, self.disp)
+    def _tensors(self, s):
+        for v in s.values():
+            if isinstance(v, dict):
+                yield from (t for t in v.values() if t is not None)
+            else:
+                yield v
 
-    def combine(self):
-        self.moe.moe_combine(self.shape, self.y, self.idx, self.w, self.disp["send_row"], self.out)
+    def op(self, name, s):
+        moe, cfg = self.moe, self.cfg
+        if name == "layout":
+            moe.run_layout(self.shape, s["idx"], s["lay"])
+        elif name == "dispatch":
+            moe.run_dispatch(self.shape, cfg.dispatch_dtype, s["x"], s["idx"], s["w"], s["lay"], s["disp"])
+        else:
+            moe.moe_combine(self.shape, s["y"], s["idx"], s["w"], s["disp"]["send_row"], s["out"])
 
     def time_steps(self, steps: int, warmup: int):
         torch = self.torch
-        for _ in range(warmup):
-            self.layout()
-            self.dispatch()
-            self.combine()
+        n = len(self.sets)
+        for i in range(warmup):
+            for name in OPS:
+                self.op(name, self.sets[i % n])
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            e = ev[i]
+            s, e = self.sets[i % n], ev[i]
             e[0].record()
-            self.layout()
+            self.op("layout", s)
             e[1].record()
-            self.dispatch()
+            self.op("dispatch", s)
             e[2].record()
-            self.combine()
+            self.op("combine", s)
             e[3].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = {"layout": [], "dispatch": [], "combine": [], "step": []}
-        for e in ev:
-            per["layout"].append(e[0].elapsed_time(e[1]))
-            per["dispatch"].append(e[1].elapsed_time(e[2]))
-            per["combine"].append(e[2].elapsed_time(e[3]))
-            per["step"].append(e[0].elapsed_time(e[3]))
+        per = {name: [e[i].elapsed_time(e[i + 1]) for e in ev] for i, name in enumerate(OPS)}
         return wall, per
 
+    def time_kernels(self, reps: int = 20, repeats: int = 5) -> dict:
+        """Per-op µs from HIP graphs of `reps` back-to-back launches over the rotating sets."""
+        torch = self.torch
+        stream = torch.cuda.Stream()
+        out = {}
+        for name in OPS:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                for s in self.sets:
+                    self.op(name, s)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=stream):
+                    for r in range(reps):
+                        self.op(name, self.sets[r % len(self.sets)])
+            g.replay()
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(repeats):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(stream):
+                    e0.record()
+                    g.replay()
+                    e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e3 / reps)
+            out[name] = sorted(times)[len(times) // 2]
+            del g
+        return out
 
-def op_summary(bytes_: int, times_ms) -> dict:
+
+def op_summary(bytes_: int, times_ms, kernel_us: float) -> dict:
     import numpy as np
 
     t = np.asarray(times_ms)
@@ -144,8 +198,10 @@ def op_summary(bytes_: int, times_ms) -> dict:
         "us_median": round(float(np.median(t) * 1e3), 3),
         "us_p10": round(float(np.percentile(t, 10) * 1e3), 3),
         "us_p90": round(float(np.percentile(t, 90) * 1e3), 3),
+        "us_kernel": round(kernel_us, 3),
         "bytes": int(bytes_),
         "GB_per_s": round(bytes_ / (mean_us * 1e-6) / 1e9, 2),
+        "GB_per_s_kernel": round(bytes_ / (kernel_us * 1e-6) / 1e9, 2),
         "frac_of_hbm_peak": round(bytes_ / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
     }
 
@@ -185,6 +241,17 @@ def cpu_baseline(cfg, W, budget_s: float = 20.0) -> dict:
     }
 
 
+def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3) -> None:
+    """A plain device copy of known size, so counter runs can scale FETCH/WRITE_SIZE."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +260,8 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--secondary", default="decode", help="second workload measured in the same run ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true", help="skip the graph-replay per-op timing")
+    ap.add_argument("--copy-calibration", action="store_true", help="also run a 1 GiB device copy (counter runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -210,23 +279,26 @@ def main() -> int:
         return 2
     torch.cuda.set_device(0)
 
-    def measure(name: str, steps: int, warmup: int) -> dict:
+    def measure(name: str) -> dict:
         cfg = W.CONFIG_BY_NAME[name]
         log(f"building workload {name}")
         wl = Workload(cfg, torch, moe, W)
-        log(f"timing {steps} steps of {name} (N_recv={wl.n_recv})")
-        wall, per = wl.time_steps(steps, warmup)
-        ops = {op: op_summary(wl.bytes[op], per[op]) for op in ("layout", "dispatch", "combine")}
-        step_bytes = sum(wl.bytes.values())
-        ms_step = wall * 1e3 / steps
-        return {"cfg": cfg, "n_recv": wl.n_recv, "ops": ops, "ms_per_step": ms_step,
-                "event_ms_per_step": float(sum(per["step"]) / steps), "step_bytes": step_bytes}
+        log(f"timing {args.steps} steps of {name} (N_recv={wl.n_recv}, {len(wl.sets)} rotating sets "
+            f"of {wl.footprint / 2**20:.0f} MiB)")
+        wall, per = wl.time_steps(args.steps, args.warmup)
+        kern = {o: float("nan") for o in OPS} if args.no_kernel_timing else wl.time_kernels()
+        ops = {o: op_summary(wl.bytes[o], per[o], kern[o]) for o in OPS}
+        res = {"cfg": cfg, "n_recv": wl.n_recv, "ops": ops, "ms_per_step": wall * 1e3 / args.steps,
+               "step_bytes": sum(wl.bytes.values()), "sets": len(wl.sets)}
+        del wl
+        torch.cuda.empty_cache()
+        return res
 
-    main_res = measure(args.workload, args.steps, args.warmup)
+    main_res = measure(args.workload)
     cfg = main_res["cfg"]
-    sec = None
-    if args.secondary and args.secondary != args.workload:
-        sec = measure(args.secondary, args.steps, args.warmup)
+    sec = measure(args.secondary) if args.secondary and args.secondary != args.workload else None
+    if args.copy_calibration:
+        copy_calibration(torch)
 
     ops = main_res["ops"]
     dom = max(("dispatch", "combine"), key=lambda o: ops[o]["us_mean"])
@@ -258,7 +330,8 @@ def main() -> int:
                                f"top-{cfg.num_topk} R={cfg.num_ranks} {cfg.dispatch_dtype} dispatch, "
                                f"fp32-accumulate combine to bf16",
                    "num_tokens": cfg.num_tokens, "hidden": cfg.hidden, "num_experts": cfg.num_experts,
-                   "num_topk": cfg.num_topk, "num_ranks": cfg.num_ranks, "n_recv": main_res["n_recv"]},
+                   "num_topk": cfg.num_topk, "num_ranks": cfg.num_ranks, "n_recv": main_res["n_recv"],
+                   "rotating_sets": main_res["sets"]},
         "ops": ops,
         "roofline": roofline,
         "cpu_baseline": cpu,

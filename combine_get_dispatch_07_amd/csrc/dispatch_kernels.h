@@ -104,6 +104,8 @@ __global__ __launch_bounds__(kDispatchBlock) void dispatch_kernel(DispatchArgs a
   const uint64_t lm = tt < a.T ? a.token_ranks[tt] : 0ull;
   const uint64_t mine = readlane64(lm, tl) & a.rank_bits;
   const uint64_t lanes_below = tl == 0 ? 0ull : (~0ull >> (kWave - tl));
+  // Lane r < R: first receive row of this chunk in rank r's segment.
+  const int chunk_row = lane < a.R ? a.ws_rank_offsets[lane] + a.chunk_base[lane * a.NC + chunk] : 0;
 
   // Load this lane's U 16-byte pieces of the slice (8 bf16 channels each).
   const int c0 = s * (U * kWave) + lane;
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(kDispatchBlock) void dispatch_kernel(DispatchArgs a
     const int r = __builtin_ctzll(todo);
     todo &= todo - 1;
     const uint64_t before = __ballot((lm >> r) & 1ull) & lanes_below;
-    const int row = a.ws_rank_offsets[r] + a.chunk_base[r * a.NC + chunk] + __popcll(before);
+    const int row = __builtin_amdgcn_readlane(chunk_row, r) + __popcll(before);
     if ((unsigned)row >= (unsigned)a.capacity) continue;  // only a plan from another layout gets here
     my_row = lane == r ? row : my_row;
 

@@ -18,7 +18,7 @@
 namespace moe {
 
 constexpr int kLayoutBlock = 256;      // tokens per block, multi-block path
-constexpr int kFusedMaxTokens = 1024;  // up to this many tokens: one block does everything
+constexpr int kFusedMaxTokens = 1024;  // up to this many tokens one block does everything
 constexpr int kFusedMaxChunks = kFusedMaxTokens / kWave;
 
 struct LayoutArgs {
@@ -33,6 +33,7 @@ struct LayoutArgs {
   uint64_t rank_magic;
   int T, k, E, R, NC, NB;
   int mask_words;          // 1: mask rows written as 32-bit words (R % 4 == 0, aligned)
+  int ids_vec4;            // 1: id rows read as 16-byte vectors (k % 4 == 0, 16-byte aligned)
 };
 
 // Rank bitmask of token t; valid expert ids are added to the LDS histogram.
@@ -40,11 +41,26 @@ __device__ __forceinline__ uint64_t token_rank_mask(const LayoutArgs& a, int t, 
   uint64_t m = 0;
   if (t < a.T) {
     const int32_t* row = a.topk_idx + (size_t)t * a.k;
-    for (int j = 0; j < a.k; ++j) {
-      const int e = row[j];
-      if ((unsigned)e < (unsigned)a.E) {
-        m |= 1ull << rank_of(e, a.rank_magic);
-        atomicAdd(&hist[e], 1);
+    if (a.ids_vec4) {  // rows are 16-byte aligned: 4 ids per load
+      const int4* row4 = reinterpret_cast<const int4*>(row);
+      for (int j = 0; j < (a.k >> 2); ++j) {
+        const int4 q = row4[j];
+        const int e4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if ((unsigned)e4[i] < (unsigned)a.E) {
+            m |= 1ull << rank_of(e4[i], a.rank_magic);
+            atomicAdd(&hist[e4[i]], 1);
+          }
+        }
+      }
+    } else {
+      for (int j = 0; j < a.k; ++j) {
+        const int e = row[j];
+        if ((unsigned)e < (unsigned)a.E) {
+          m |= 1ull << rank_of(e, a.rank_magic);
+          atomicAdd(&hist[e], 1);
+        }
       }
     }
   }
@@ -85,10 +101,11 @@ __device__ __forceinline__ void publish_rank_offsets(const LayoutArgs& a, const 
   if (lane == a.R - 1) a.ws_rank_offsets[a.R] = incl;
 }
 
-// T <= kFusedMaxTokens: a single block of ceil(T/64) waves (at least one).
+// T <= kFusedMaxTokens: one block of ceil(T/64) waves (at least one) does
+// everything in one launch.  Dynamic LDS: hist[E]; static: chunk counts [R][16].
 __global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArgs a) {
-  extern __shared__ int hist[];  // [E]
-  __shared__ int chunk_cnt[kWave * kFusedMaxChunks];  // [R][16]
+  extern __shared__ int hist[];
+  __shared__ int chunk_cnt[kWave * kFusedMaxChunks];
   __shared__ int rank_total[kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   for (int e = tid; e < a.E; e += blockDim.x) hist[e] = 0;
@@ -104,7 +121,7 @@ __global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArg
   __syncthreads();
 
   for (int e = tid; e < a.E; e += blockDim.x) a.tokens_per_expert[e] = hist[e];
-  if (tid < a.R) {
+  if (tid < a.R) {  // at most 16 chunks: a serial scan per rank is shortest
     int run = 0;
     for (int c = 0; c < a.NC; ++c) {
       a.chunk_base[tid * a.NC + c] = run;

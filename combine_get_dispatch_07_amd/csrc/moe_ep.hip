@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 
@@ -22,8 +23,9 @@ constexpr int kMaxTopk = 32;
 constexpr int kMaxRanks = 64;
 constexpr int kMaxExperts = 4096;
 constexpr size_t kPlanAlign = 256;
-// Enough waves to keep every SIMD of the 256 CUs busy several times over.
-constexpr long kTargetWaves = 8192;
+constexpr int kMaxDevices = 64;
+// Wide FP8 dispatch slices only when they still give this many waves.
+constexpr long kMinFp8Waves = 4096;
 
 struct PlanLayout {
   size_t token_ranks, chunk_base, block_expert, rank_offsets, total;
@@ -72,16 +74,19 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // A pointer may be NULL exactly when the array it stands for is empty.
 bool present(const void* p, int64_t elements) { return p != nullptr || elements == 0; }
 
-// Chunks of 8 channels per lane per work item, from the instantiated set.
-// Fewer, wider items amortise the per-item slot arithmetic; narrower ones
-// give small batches enough waves to fill the chip.
-int pick_chunks_per_lane(int T, int H8) {
-  static const int kOptions[] = {14, 7, 4, 2, 1};
+// Dispatch work item = (token, slice of U*512 channels).  bf16 rows favour
+// narrow slices (many short waves keep the most stores in flight).  FP8 rows
+// favour wide slices when there are enough tokens to fill the chip: one wave
+// then quantises the whole row and writes each destination's scale row as a
+// unit instead of 16-byte fragments from many waves.
+int pick_dispatch_chunks_per_lane(int T, int H8, bool fp8) {
+  if (!fp8) return 1;
+  static const int kOptions[] = {14, 7, 4, 2};
   const int groups = (H8 + moe::kWave - 1) / moe::kWave;  // 64-lane chunk groups per row
   for (int u : kOptions) {
     if (u > groups) continue;
     const long slices = (groups + u - 1) / u;
-    if ((long)T * slices >= kTargetWaves) return u;
+    if ((long)T * slices >= kMinFp8Waves) return u;
   }
   return 1;
 }
@@ -102,8 +107,38 @@ void launch_dispatch(int U, dim3 grid, hipStream_t stream, const moe::DispatchAr
   }
 }
 
+#ifndef MOE_COMBINE_PERSISTENT
+#define MOE_COMBINE_PERSISTENT 1
+#endif
+// Resident combine waves per CU in the persistent launch (4 per SIMD).
+#ifndef MOE_COMBINE_WAVES_PER_CU
+#define MOE_COMBINE_WAVES_PER_CU 16
+#endif
+
+// Compute units of the current device, queried once per device.
+int device_cu_count() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 void launch_combine(int U, dim3 grid, hipStream_t stream, const moe::CombineArgs& a) {
   const dim3 block(moe::kCombineBlock);
+  if (MOE_COMBINE_PERSISTENT) {
+    const long waves = (long)device_cu_count() * MOE_COMBINE_WAVES_PER_CU;
+    const dim3 pgrid((unsigned)std::min<long>(grid.x, waves / (moe::kCombineBlock / moe::kWave)));
+    switch (U) {
+      case 2: hipLaunchKernelGGL((moe::combine_persistent_kernel<2>), pgrid, block, 0, stream, a); break;
+      default: hipLaunchKernelGGL((moe::combine_persistent_kernel<1>), pgrid, block, 0, stream, a); break;
+    }
+    return;
+  }
   switch (U) {
     case 4: hipLaunchKernelGGL((moe::combine_kernel<4>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((moe::combine_kernel<2>), grid, block, 0, stream, a); break;
@@ -171,6 +206,7 @@ moe_status moe_get_dispatch_layout(const moe_shape* shape, const int32_t* topk_i
   a.NC = p.NC;
   a.NB = p.NB;
   a.mask_words = (s.num_ranks % 4 == 0 && aligned(is_token_in_rank, 4)) ? 1 : 0;
+  a.ids_vec4 = (s.num_topk % 4 == 0 && aligned(topk_idx, 16)) ? 1 : 0;
   const size_t hist_bytes = (size_t)s.num_experts * sizeof(int);
 
   if (s.num_tokens <= moe::kFusedMaxTokens) {
@@ -241,7 +277,7 @@ moe_status moe_dispatch(const moe_shape* shape, moe_dtype dtype, const void* x,
 #ifdef MOE_FORCE_DISPATCH_U
   const int U = MOE_FORCE_DISPATCH_U;
 #else
-  const int U = pick_chunks_per_lane(s.num_tokens, a.H8);
+  const int U = pick_dispatch_chunks_per_lane(s.num_tokens, a.H8, fp8);
 #endif
   const int groups = (a.H8 + moe::kWave - 1) / moe::kWave;
   a.slices = (groups + U - 1) / U;
@@ -289,7 +325,7 @@ moe_status moe_combine(const moe_shape* shape, const void* y, int32_t num_y_rows
 #ifdef MOE_FORCE_COMBINE_U
   const int U = MOE_FORCE_COMBINE_U;
 #else
-  const int U = std::min(2, pick_chunks_per_lane(s.num_tokens, a.H8));
+  const int U = 1;
 #endif
   const int groups = (a.H8 + moe::kWave - 1) / moe::kWave;
   a.slices = (groups + U - 1) / U;
