@@ -21,6 +21,11 @@ namespace moe {
 #ifndef MOE_COMBINE_NT_LOADS
 #define MOE_COMBINE_NT_LOADS 0
 #endif
+// Output rows are written once and not re-read here: nontemporal stores keep
+// them from displacing expert-output lines in L2 (measured faster).
+#ifndef MOE_COMBINE_NT_STORE
+#define MOE_COMBINE_NT_STORE 1
+#endif
 
 constexpr int kCombineBlock = 256;
 constexpr int kSlotBatch = 8;
@@ -215,6 +220,136 @@ __global__ __launch_bounds__(kCombineBlock) void combine_persistent_kernel(Combi
         orow[c] = o;
       }
     }
+  }
+}
+
+// Two-deep software pipeline for k <= 8 (one slot batch) and num_y_rows >= 1.
+// Vector loads retire in order against one counter, so per item i the loop
+// issues, in this order: (1) the metadata of item i+2, (2) the payload of item
+// i+1; then it waits only for item i's payload (accumulate, store) and for item
+// i+2's metadata (resolve its rows), while item i+1's payload stays in flight.
+// For the wait counts to be exact on every path, every load is issued
+// unconditionally from a clamped, always valid address and masked afterwards,
+// and the two payload buffers alternate by unrolling instead of being copied.
+struct SlotRows {
+  int row[kSlotBatch];
+  float w[kSlotBatch];
+};
+
+struct RawMeta {
+  int id, rr;
+  float w;
+};
+
+__device__ __forceinline__ RawMeta load_raw_meta(const CombineArgs& a, int item, int lane) {
+  const int t = min(item, a.items - 1) / a.slices;
+  RawMeta m;
+  m.id = a.topk_idx[(size_t)t * a.k + min(lane, a.k - 1)];
+  m.w = a.topk_w[(size_t)t * a.k + min(lane, a.k - 1)];
+  m.rr = a.send_row[(size_t)t * a.R + min(lane, a.R - 1)];
+  return m;
+}
+
+__device__ __forceinline__ SlotRows resolve_rows(const CombineArgs& a, const RawMeta& m, int item, int lane) {
+  const bool valid = item < a.items && lane < a.k && (unsigned)m.id < (unsigned)a.E;
+  const int rank = valid ? rank_of(m.id, a.rank_magic) : 0;
+  int row = __shfl(m.rr, rank, kWave);
+  row = valid && (unsigned)row < (unsigned)a.num_y_rows ? row : -1;
+  SlotRows r;
+#pragma unroll
+  for (int j = 0; j < kSlotBatch; ++j) {
+    r.row[j] = __builtin_amdgcn_readlane(row, j);
+    r.w[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m.w), j));
+  }
+  return r;
+}
+
+template <int U>
+__device__ __forceinline__ void load_payload(const CombineArgs& a, const SlotRows& r, int item, int lane,
+                                             u32x4 (&v)[kSlotBatch][U]) {
+  const int c0 = (min(item, a.items - 1) % a.slices) * (U * kWave) + lane;
+#pragma unroll
+  for (int j = 0; j < kSlotBatch; ++j) {
+    const u32x4* yrow = reinterpret_cast<const u32x4*>(a.y + (size_t)max(r.row[j], 0) * a.H);
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[j][u] = yrow[min(c0 + u * kWave, a.H8 - 1)];
+  }
+}
+
+// One pipeline stage: see the comment above.  `pc` holds item's payload,
+// `pn` receives item + nw's; on return cur/nxt have advanced by one item.
+template <int U>
+__device__ __forceinline__ void combine_stage(const CombineArgs& a, int item, int nw, int lane, SlotRows& cur,
+                                              SlotRows& nxt, const u32x4 (&pc)[kSlotBatch][U],
+                                              u32x4 (&pn)[kSlotBatch][U]) {
+#pragma clang fp contract(off)
+  const RawMeta m2 = load_raw_meta(a, item + 2 * nw, lane);
+  load_payload<U>(a, nxt, item + nw, lane, pn);
+
+  const int t = item / a.slices;
+  const int c0 = (item - t * a.slices) * (U * kWave) + lane;
+  float acc[U][8];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kSlotBatch; ++j) {
+    if (cur.row[j] >= 0) {
+      const float wj = cur.w[j];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = wj * bf16_lo(pc[j][u][i]);
+          const float p1 = wj * bf16_hi(pc[j][u][i]);
+          acc[u][2 * i] = acc[u][2 * i] + p0;
+          acc[u][2 * i + 1] = acc[u][2 * i + 1] + p1;
+        }
+      }
+    }
+  }
+  u32x4* orow = reinterpret_cast<u32x4*>(a.out + (size_t)t * a.H);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = c0 + u * kWave;
+    if (c < a.H8) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = f32_to_bf16_rne(acc[u][2 * i]) | (f32_to_bf16_rne(acc[u][2 * i + 1]) << 16);
+#if MOE_COMBINE_NT_STORE
+      __builtin_nontemporal_store(o, orow + c);
+#else
+      orow[c] = o;
+#endif
+    }
+  }
+  cur = nxt;
+  nxt = resolve_rows(a, m2, item + 2 * nw, lane);
+}
+
+template <int U>
+__global__ __launch_bounds__(kCombineBlock) void combine_pipelined_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = gridDim.x * (kCombineBlock / kWave);
+  int item = blockIdx.x * (kCombineBlock / kWave) + wave;
+  if (item >= a.items) return;
+
+  const RawMeta m0 = load_raw_meta(a, item, lane);
+  const RawMeta m1 = load_raw_meta(a, item + nw, lane);
+  SlotRows cur = resolve_rows(a, m0, item, lane);
+  u32x4 buf_a[kSlotBatch][U], buf_b[kSlotBatch][U];
+  load_payload<U>(a, cur, item, lane, buf_a);
+  SlotRows nxt = resolve_rows(a, m1, item + nw, lane);
+  for (;;) {
+    combine_stage<U>(a, item, nw, lane, cur, nxt, buf_a, buf_b);
+    item += nw;
+    if (item >= a.items) break;
+    combine_stage<U>(a, item, nw, lane, cur, nxt, buf_b, buf_a);
+    item += nw;
+    if (item >= a.items) break;
   }
 }
 

@@ -110,9 +110,13 @@ void launch_dispatch(int U, dim3 grid, hipStream_t stream, const moe::DispatchAr
 #ifndef MOE_COMBINE_PERSISTENT
 #define MOE_COMBINE_PERSISTENT 1
 #endif
-// Resident combine waves per CU in the persistent launch (4 per SIMD).
+#ifndef MOE_COMBINE_PIPELINED
+#define MOE_COMBINE_PIPELINED 1
+#endif
+// Resident combine waves per CU in the persistent launch (2 per SIMD, each
+// with two items' payload in flight).
 #ifndef MOE_COMBINE_WAVES_PER_CU
-#define MOE_COMBINE_WAVES_PER_CU 16
+#define MOE_COMBINE_WAVES_PER_CU 8
 #endif
 
 // Compute units of the current device, queried once per device.
@@ -133,6 +137,10 @@ void launch_combine(int U, dim3 grid, hipStream_t stream, const moe::CombineArgs
   if (MOE_COMBINE_PERSISTENT) {
     const long waves = (long)device_cu_count() * MOE_COMBINE_WAVES_PER_CU;
     const dim3 pgrid((unsigned)std::min<long>(grid.x, waves / (moe::kCombineBlock / moe::kWave)));
+    if (MOE_COMBINE_PIPELINED && a.k <= moe::kSlotBatch && a.num_y_rows >= 1) {
+      hipLaunchKernelGGL((moe::combine_pipelined_kernel<1>), pgrid, block, 0, stream, a);
+      return;
+    }
     switch (U) {
       case 2: hipLaunchKernelGGL((moe::combine_persistent_kernel<2>), pgrid, block, 0, stream, a); break;
       default: hipLaunchKernelGGL((moe::combine_persistent_kernel<1>), pgrid, block, 0, stream, a); break;
