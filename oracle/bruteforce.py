@@ -162,3 +162,54 @@ def combine(y_bits: np.ndarray, topk_idx: List[List[int]], topk_w: List[List[flo
             row_out.append(bf16_round(acc))
         out.append(row_out)
     return out
+
+
+def ll_dispatch(x_bits: np.ndarray, topk_idx: List[List[int]], E: int, capacity: int, dtype: str) -> Dict[str, object]:
+    """Per-expert buffers: walk tokens in order and append each to every distinct valid expert it names."""
+    T = len(topk_idx)
+    H = x_bits.shape[1] if T else 0
+    count = [0] * E
+    slot_pos = []
+    src = [[-1] * capacity for _ in range(E)]
+    rows: Dict[tuple, List[int]] = {}
+    scales: Dict[tuple, List[float]] = {}
+    for t in range(T):
+        placed: Dict[int, int] = {}
+        for e in topk_idx[t]:
+            if 0 <= e < E and e not in placed:
+                placed[e] = count[e]
+                count[e] += 1
+        slot_pos.append([placed[e] if 0 <= e < E else -1 for e in topk_idx[t]])
+        for e, p in placed.items():
+            src[e][p] = t
+            if dtype == "bf16":
+                rows[(e, p)] = [int(b) for b in x_bits[t]]
+            else:
+                q_row, s_row = [], []
+                for b0 in range(0, H, 128):
+                    vals = [bf16_value(int(b)) for b in x_bits[t, b0:b0 + 128]]
+                    a = max(abs(v) for v in vals)
+                    s = fl32(max(a, fl32(1e-4)) / 448.0)
+                    s_row.append(s)
+                    q_row.extend(e4m3_round(fl32(v / s)) for v in vals)
+                rows[(e, p)] = q_row
+                scales[(e, p)] = s_row
+    return {"recv_count": count, "slot_pos": slot_pos, "recv_src_idx": src, "rows": rows, "scales": scales}
+
+
+def ll_combine(y_bits: np.ndarray, topk_idx: List[List[int]], topk_w: List[List[float]],
+               slot_pos: List[List[int]]) -> List[List[int]]:
+    H = y_bits.shape[2]
+    out = []
+    for t in range(len(topk_idx)):
+        row_out = []
+        for c in range(H):
+            acc = 0.0
+            for j, e in enumerate(topk_idx[t]):
+                p = slot_pos[t][j]
+                if p < 0:
+                    continue
+                acc = fl32(acc + fl32(fl32(topk_w[t][j]) * bf16_value(int(y_bits[e, p, c]))))
+            row_out.append(bf16_round(acc))
+        out.append(row_out)
+    return out

@@ -202,6 +202,80 @@ def combine_f64(y_bits: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, se
     return acc, mag
 
 
+# ----------------------------------------------------------------------------------------------
+# Low-latency (per-expert) receive layout.
+#
+# [DeepEP overview] and [overlap notes, 节点间通信] describe a second, low-latency dispatch/combine
+# mode for decoding, whose receivers keep one fixed-size buffer per local expert.  Readings taken
+# (the pages give no more detail):
+#   8. one receive row per (token, distinct valid expert) -- a token naming an expert twice is
+#      sent to it once, and both slots read that row back in combine;
+#   9. expert e's buffer has `capacity` rows; the row of token t is
+#      pos(t, e) = #{t' < t : t' names e} (stable, ascending source token);
+#  10. combine: acc = +0, then for j ascending over valid slots,
+#      acc = fl32(acc + fl32(w_j * y[e_j, pos(t, e_j)])); out = BF16_RNE(acc).
+# Buffers are [E, capacity, ...]: rank r's experts are the contiguous block r*L .. r*L+L-1, so this
+# is also R ranks x [L, capacity, ...] as each receiving rank would hold it.
+
+def ll_layout(topk_idx: np.ndarray, num_experts: int) -> Tuple[np.ndarray, np.ndarray]:
+    """recv_count int32[E] (distinct tokens per expert) and slot_pos int32[T, k] (pos(t, e_tj) or -1)."""
+    T, k = topk_idx.shape
+    e = topk_idx.astype(np.int64)
+    valid = (e >= 0) & (e < num_experts)
+    member = np.zeros((T, num_experts), dtype=np.int64)
+    t_of_slot = np.broadcast_to(np.arange(T)[:, None], e.shape)
+    member[t_of_slot[valid], e[valid]] = 1
+    before = np.cumsum(member, axis=0) - member  # tokens t' < t that name e
+    slot_pos = np.where(valid, before[t_of_slot, np.where(valid, e, 0)], -1)
+    return member.sum(axis=0).astype(np.int32), slot_pos.astype(np.int32)
+
+
+def ll_dispatch(x_bits: np.ndarray, topk_idx: np.ndarray, num_experts: int, capacity: int, dtype: str
+                ) -> Dict[str, np.ndarray]:
+    """Per-expert receive buffers; rows at or beyond recv_count[e] are left as zeros / -1."""
+    T, H = x_bits.shape
+    recv_count, slot_pos = ll_layout(topk_idx, num_experts)
+    assert capacity >= T
+    src = np.full((num_experts, capacity), -1, dtype=np.int32)
+    tt, jj = np.nonzero(slot_pos >= 0)
+    ee = topk_idx[tt, jj].astype(np.int64)
+    src[ee, slot_pos[tt, jj]] = tt  # duplicate slots write the same (row, token)
+    out = {"recv_count": recv_count, "slot_pos": slot_pos, "recv_src_idx": src}
+    flat = src.reshape(-1)
+    rows = np.nonzero(flat >= 0)[0]
+    if dtype == "bf16":
+        rx = np.zeros((num_experts * capacity, H), dtype=np.uint16)
+        rx[rows] = x_bits[flat[rows]]
+        out["recv_x"] = rx.reshape(num_experts, capacity, H)
+    else:
+        q, sc = quantize_fp8_blocks(x_bits[flat[rows]]) if rows.size else (
+            np.zeros((0, H), np.uint8), np.zeros((0, H // FP8_BLOCK), np.float32))
+        rx = np.zeros((num_experts * capacity, H), dtype=np.uint8)
+        rs = np.zeros((num_experts * capacity, H // FP8_BLOCK), dtype=np.float32)
+        rx[rows], rs[rows] = q, sc
+        out["recv_x"] = rx.reshape(num_experts, capacity, H)
+        out["recv_scales"] = rs.reshape(num_experts, capacity, H // FP8_BLOCK)
+    return out
+
+
+def ll_combine(y_bits: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, slot_pos: np.ndarray,
+               num_experts: int, tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """Combine from per-expert buffers y[E, capacity, H] (reading 10)."""
+    E, cap, H = y_bits.shape
+    t_sel = np.arange(topk_idx.shape[0]) if tokens is None else np.asarray(tokens)
+    acc = np.zeros((t_sel.size, H), dtype=np.float32)
+    flat = y_bits.reshape(E * cap, H)
+    for j in range(topk_idx.shape[1]):
+        pos = slot_pos[t_sel, j]
+        ok = pos >= 0
+        if not ok.any():
+            continue
+        rows = topk_idx[t_sel[ok], j].astype(np.int64) * cap + pos[ok]
+        prod = (topk_w[t_sel[ok], j][:, None].astype(np.float32) * bf16_bits_to_f32(flat[rows])).astype(np.float32)
+        acc[ok] = (acc[ok] + prod).astype(np.float32)
+    return f32_to_bf16_bits_rne(acc)
+
+
 def run_all(x_bits: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, num_experts: int,
             num_ranks: int, dtype: str) -> Dict[str, np.ndarray]:
     """Layout, slots, metadata and payload for one workload, as a dict of arrays."""

@@ -11,6 +11,7 @@ import pytest
 
 from oracle import moe_oracle as O
 from oracle import numerics as N
+from tests import test_oracle_ll as PL
 from tests import test_oracle_pins as P
 
 
@@ -24,6 +25,9 @@ def _pin_suite():
     P.test_fp8_edge_rows()
     P.test_identity_round_trip_k1_is_exact()
     P.test_identity_round_trip_weighted(P.W.CONFIG_BY_NAME["tiny"])
+    PL.test_golden_low_latency()
+    for case in PL.LL_CASES[:3]:
+        PL.test_ll_vs_bruteforce(case, "bf16")
 
 
 def _rank_modulo(topk_idx, E, R):
@@ -123,7 +127,39 @@ def _meta_global_ids(idx, w, E, R, send_row, n):
     return src, np.where(ridx >= 0, ridx + rows_rank[:, None] * L, -1).astype(np.int32), rw
 
 
+def _ll_layout_per_slot(topk_idx, num_experts):
+    # positions count every slot, so a token naming an expert twice takes two rows
+    T, k = topk_idx.shape
+    e = topk_idx.astype(np.int64)
+    valid = (e >= 0) & (e < num_experts)
+    pos = np.full((T, k), -1, dtype=np.int64)
+    count = np.zeros(num_experts, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            if valid[t, j]:
+                pos[t, j] = count[e[t, j]]
+                count[e[t, j]] += 1
+    return count.astype(np.int32), pos.astype(np.int32)
+
+
+_orig_ll_combine = O.ll_combine
+
+
+def _ll_combine_once_per_expert(y, idx, w, slot_pos, E, tokens=None):
+    pos = slot_pos.copy()
+    for t in range(idx.shape[0]):
+        seen = set()
+        for j in range(idx.shape[1]):
+            if pos[t, j] >= 0:
+                if idx[t, j] in seen:
+                    pos[t, j] = -1
+                seen.add(idx[t, j])
+    return _orig_ll_combine(y, idx, w, pos, E, tokens)
+
+
 MUTANTS = {
+    "ll_positions_per_slot": ("ll_layout", _ll_layout_per_slot),
+    "ll_combine_duplicate_once": ("ll_combine", _ll_combine_once_per_expert),
     "rank_is_e_mod_R": ("expert_ranks", _rank_modulo),
     "inclusive_prefix": ("assign_slots", _slots_inclusive),
     "descending_tokens_in_segment": ("assign_slots", _slots_descending),
