@@ -21,7 +21,11 @@ Algorithmic bytes (what the method must move once; distinct rows once):
   dispatch = T*H*2 + T*k*8 + T*R + N*(H*b + S + 4 + 8*k) + T*R*4
              (b = 2, S = 0 for bf16; b = 1, S = 4*H/128 for FP8)
   combine  = N*H*2 + T*k*8 + T*R*4 + T*H*2
-with N = number of receive rows.
+with N = number of receive rows.  The low-latency (per-expert) path, also
+measured on the decode workload:
+  dispatch_ll = T*H*2 + T*k*4 + N'*(H*b + S + 4) + E*4 + T*k*4
+  combine_ll  = N'*H*2 + T*k*12 + T*H*2
+with N' = rows written into the per-expert buffers.
 """
 from __future__ import annotations
 
@@ -54,6 +58,15 @@ def algorithmic_bytes(cfg, n_recv: int) -> dict:
         "layout": T * k * 4 + T * R + 4 * (R + E),
         "dispatch": T * H * 2 + T * k * 8 + T * R + n_recv * (H * b + S + 4 + 8 * k) + T * R * 4,
         "combine": n_recv * H * 2 + T * k * 8 + T * R * 4 + T * H * 2,
+    }
+
+
+def ll_algorithmic_bytes(cfg, n_rows: int) -> dict:
+    T, H, k, E = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts
+    b, S = (1, 4 * H // 128) if cfg.dispatch_dtype == "fp8" else (2, 0)
+    return {
+        "dispatch_ll": T * H * 2 + T * k * 4 + n_rows * (H * b + S + 4) + E * 4 + T * k * 4,
+        "combine_ll": n_rows * H * 2 + T * k * 12 + T * H * 2,
     }
 
 
@@ -158,12 +171,12 @@ class Workload:
         per = {name: [e[i].elapsed_time(e[i + 1]) for e in ev] for i, name in enumerate(OPS)}
         return wall, per
 
-    def time_kernels(self, reps: int = 20, repeats: int = 5) -> dict:
+    def time_kernels(self, reps: int = 20, repeats: int = 5, ops=OPS) -> dict:
         """Per-op µs from HIP graphs of `reps` back-to-back launches over the rotating sets."""
         torch = self.torch
         stream = torch.cuda.Stream()
         out = {}
-        for name in OPS:
+        for name in ops:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.stream(stream):
                 for s in self.sets:
@@ -186,6 +199,80 @@ class Workload:
             out[name] = sorted(times)[len(times) // 2]
             del g
         return out
+
+
+class LlWorkload(Workload):
+    """The low-latency path: dispatch into per-expert buffers [E, T, H], combine from them."""
+
+    OPS_LL = ("dispatch_ll", "combine_ll")
+
+    def __init__(self, cfg, torch, moe, W, nsets=None):
+        import numpy as np
+
+        self.cfg, self.torch, self.moe = cfg, torch, moe
+        d = W.make_inputs(cfg)
+        self.shape = moe.MoeShape(cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks)
+        x16 = torch.from_numpy(d["x"].view(np.int16))
+        first = self._new_ll_set(x16, d)
+        moe.run_dispatch_ll(self.shape, cfg.dispatch_dtype, first["x"], first["idx"], first["ll"])
+        torch.cuda.synchronize()
+        count = first["ll"]["recv_count"].cpu().numpy()
+        self.n_recv = int(count.sum())
+        # expert outputs ~ N(0,1) in the rows that were received, zeros elsewhere
+        rows = W.draw_expert_outputs(W.y_stream(cfg), self.n_recv, cfg.hidden)
+        y = np.zeros((cfg.num_experts, cfg.num_tokens, cfg.hidden), np.uint16)
+        i = 0
+        for e, n in enumerate(count):
+            y[e, :n] = rows[i:i + n]
+            i += n
+        y16 = torch.from_numpy(y.view(np.int16))
+        first["y"] = y16.cuda().view(torch.bfloat16)
+        self.bytes = ll_algorithmic_bytes(cfg, self.n_recv)
+        footprint = sum(t.numel() * t.element_size() for t in self._tensors(first))
+        if nsets is None:
+            nsets = max(2, min(16, -(-ROTATION_BYTES // footprint)))
+        self.sets = [first]
+        for _ in range(nsets - 1):
+            s_ = self._new_ll_set(x16, d)
+            s_["y"] = y16.cuda().view(torch.bfloat16)
+            self.sets.append(s_)
+        self.footprint = footprint
+
+    def _new_ll_set(self, x16, d):
+        torch, moe, cfg = self.torch, self.moe, self.cfg
+        return {
+            "x": x16.cuda().view(torch.bfloat16),
+            "idx": torch.from_numpy(d["topk_idx"]).cuda(),
+            "w": torch.from_numpy(d["topk_w"]).cuda(),
+            "ll": moe.alloc_dispatch_ll(self.shape, cfg.dispatch_dtype),
+            "out": torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda"),
+        }
+
+    def op(self, name, s):
+        if name == "dispatch_ll":
+            self.moe.run_dispatch_ll(self.shape, self.cfg.dispatch_dtype, s["x"], s["idx"], s["ll"])
+        else:
+            self.moe.moe_combine_ll(self.shape, s["y"], s["idx"], s["w"], s["ll"]["slot_pos"], s["out"])
+
+    def time_ll(self, steps: int, warmup: int):
+        torch = self.torch
+        n = len(self.sets)
+        for i in range(warmup):
+            for name in self.OPS_LL:
+                self.op(name, self.sets[i % n])
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            s_, e = self.sets[i % n], ev[i]
+            e[0].record()
+            self.op("dispatch_ll", s_)
+            e[1].record()
+            self.op("combine_ll", s_)
+            e[2].record()
+        torch.cuda.synchronize()
+        per = {name: [e[i].elapsed_time(e[i + 1]) for e in ev] for i, name in enumerate(self.OPS_LL)}
+        kern = self.time_kernels(ops=self.OPS_LL)
+        return {o: op_summary(self.bytes[o], per[o], kern[o]) for o in self.OPS_LL}
 
 
 def op_summary(bytes_: int, times_ms, kernel_us: float) -> dict:
@@ -262,6 +349,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the graph-replay per-op timing")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a 1 GiB device copy (counter runs)")
+    ap.add_argument("--no-low-latency", action="store_true", help="skip the per-expert path on decode")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -292,6 +380,12 @@ def main() -> int:
                "step_bytes": sum(wl.bytes.values()), "sets": len(wl.sets)}
         del wl
         torch.cuda.empty_cache()
+        if cfg.name == "decode" and not args.no_low_latency:
+            log(f"timing the low-latency path on {name}")
+            ll = LlWorkload(cfg, torch, moe, W)
+            res["low_latency"] = {"n_rows": ll.n_recv, "ops": ll.time_ll(args.steps, args.warmup)}
+            del ll
+            torch.cuda.empty_cache()
         return res
 
     main_res = measure(args.workload)
@@ -342,6 +436,10 @@ def main() -> int:
                                          f"top-{c2.num_topk} R={c2.num_ranks} {c2.dispatch_dtype} dispatch",
                              "n_recv": sec["n_recv"], "ms_per_step": round(sec["ms_per_step"], 4),
                              "ops": sec["ops"]}
+        if "low_latency" in sec:
+            line["secondary"]["low_latency"] = sec["low_latency"]
+    if "low_latency" in main_res:
+        line["low_latency"] = main_res["low_latency"]
     print(json.dumps(line), flush=True)
     return 0
 

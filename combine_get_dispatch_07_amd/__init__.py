@@ -13,8 +13,9 @@ from typing import Dict, Optional
 
 import torch
 
-from ._lib import (LIB_PATH, MoeError, MoeShape, max_recv_rows, moe_combine, moe_dispatch,  # noqa: F401
-                   moe_get_dispatch_layout, status_string, workspace_bytes)
+from ._lib import (LIB_PATH, MoeError, MoeShape, ll_workspace_bytes, max_recv_rows, moe_combine,  # noqa: F401
+                   moe_combine_ll, moe_dispatch, moe_dispatch_ll, moe_get_dispatch_layout, status_string,
+                   workspace_bytes)
 
 
 def alloc_layout(shape: MoeShape, device="cuda") -> Dict[str, torch.Tensor]:
@@ -54,3 +55,25 @@ def run_dispatch(shape: MoeShape, dtype: str, x: torch.Tensor, topk_idx: torch.T
     moe_dispatch(shape, dtype, x, topk_idx, topk_w, lay["workspace"], d["recv_x"], d["recv_scales"],
                  d["recv_src_idx"], d["recv_topk_idx"], d["recv_topk_w"], d["rank_offsets"], d["send_row"],
                  d["num_recv"], stream)
+
+
+def alloc_dispatch_ll(shape: MoeShape, dtype: str, device="cuda", capacity: Optional[int] = None
+                      ) -> Dict[str, torch.Tensor]:
+    """Outputs and workspace of moe_dispatch_ll; per-expert capacity defaults to T."""
+    cap = shape.num_tokens if capacity is None else capacity
+    E, H = shape.num_experts, shape.hidden
+    fp8 = dtype == "fp8"
+    return {
+        "recv_x": torch.empty((E, cap, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=device),
+        "recv_scales": torch.empty((E, cap, H // 128), dtype=torch.float32, device=device) if fp8 else None,
+        "recv_src_idx": torch.empty((E, cap), dtype=torch.int32, device=device),
+        "recv_count": torch.empty(E, dtype=torch.int32, device=device),
+        "slot_pos": torch.empty((shape.num_tokens, shape.num_topk), dtype=torch.int32, device=device),
+        "workspace": torch.empty(ll_workspace_bytes(shape), dtype=torch.uint8, device=device),
+    }
+
+
+def run_dispatch_ll(shape: MoeShape, dtype: str, x: torch.Tensor, topk_idx: torch.Tensor,
+                    d: Dict[str, torch.Tensor], stream=None) -> None:
+    moe_dispatch_ll(shape, dtype, x, topk_idx, d["workspace"], d["recv_x"], d["recv_scales"], d["recv_src_idx"],
+                    d["recv_count"], d["slot_pos"], stream)

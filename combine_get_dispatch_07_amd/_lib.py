@@ -70,6 +70,12 @@ def _load() -> ctypes.CDLL:
     lib.moe_dispatch.restype = ctypes.c_int
     lib.moe_combine.argtypes = [SH, P, I32, P, P, P, P, P]
     lib.moe_combine.restype = ctypes.c_int
+    lib.moe_ll_workspace_bytes.argtypes = [SH]
+    lib.moe_ll_workspace_bytes.restype = SZ
+    lib.moe_dispatch_ll.argtypes = [SH, ctypes.c_int, P, P, P, SZ, I32, P, P, P, P, P, P]
+    lib.moe_dispatch_ll.restype = ctypes.c_int
+    lib.moe_combine_ll.argtypes = [SH, P, I32, P, P, P, P, P]
+    lib.moe_combine_ll.restype = ctypes.c_int
     return lib
 
 
@@ -86,6 +92,10 @@ def workspace_bytes(shape: MoeShape) -> int:
 
 def max_recv_rows(shape: MoeShape) -> int:
     return int(lib.moe_max_recv_rows(ctypes.byref(shape.c())))
+
+
+def ll_workspace_bytes(shape: MoeShape) -> int:
+    return int(lib.moe_ll_workspace_bytes(ctypes.byref(shape.c())))
 
 
 def _stream(stream) -> Optional[int]:
@@ -155,3 +165,28 @@ def moe_combine(shape: MoeShape, y, topk_idx, topk_w, send_row, out, stream=None
         _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
         _ptr(send_row, "send_row", torch.int32, T * R), _ptr(out, "out", torch.bfloat16, T * H), _stream(stream))
     _check("moe_combine", code)
+
+
+def moe_dispatch_ll(shape: MoeShape, dtype: str, x, topk_idx, workspace, recv_x, recv_scales, recv_src_idx,
+                    recv_count, slot_pos, stream=None) -> None:
+    T, H, k, E = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts
+    fp8 = DTYPES[dtype] == MOE_FP8_E4M3
+    cap = recv_src_idx.shape[1] if recv_src_idx.dim() == 2 else recv_src_idx.numel() // max(E, 1)
+    code = lib.moe_dispatch_ll(
+        ctypes.byref(shape.c()), DTYPES[dtype], _ptr(x, "x", torch.bfloat16, T * H),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(workspace, "workspace", torch.uint8),
+        workspace.numel(), cap, _ptr(recv_x, "recv_x", torch.uint8 if fp8 else torch.bfloat16, E * cap * H),
+        _ptr(recv_scales, "recv_scales", torch.float32, E * cap * (H // 128)) if fp8 else None,
+        _ptr(recv_src_idx, "recv_src_idx", torch.int32, E * cap), _ptr(recv_count, "recv_count", torch.int32, E),
+        _ptr(slot_pos, "slot_pos", torch.int32, T * k), _stream(stream))
+    _check("moe_dispatch_ll", code)
+
+
+def moe_combine_ll(shape: MoeShape, y, topk_idx, topk_w, slot_pos, out, stream=None) -> None:
+    T, H, k, E = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts
+    cap = y.shape[1]
+    code = lib.moe_combine_ll(
+        ctypes.byref(shape.c()), _ptr(y, "y", torch.bfloat16, E * cap * H), cap,
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
+        _ptr(slot_pos, "slot_pos", torch.int32, T * k), _ptr(out, "out", torch.bfloat16, T * H), _stream(stream))
+    _check("moe_combine_ll", code)

@@ -1,0 +1,189 @@
+// Low-latency (per-expert) receive layout: dispatch into one fixed-capacity
+// buffer per expert, [E, cap, H], as the low-latency decode mode of the DeepEP
+// pages keeps one buffer per local expert ("DeepEP：面向MoE的高吞吐低延迟GPU通信库",
+// ssnai.com; "DeepEP：年度总结中的计算通信重叠摘记", notes.kuangjux.top, section
+// 节点间通信).  One receive row per (token, distinct valid expert); the row of
+// token t in expert e's buffer is the number of earlier tokens naming e.
+//
+// Positions are computed without any ordering race: a wave owns 64 tokens and
+// builds, in LDS, one 64-bit membership mask per expert (atomicOr is order-
+// independent); a token's position inside its chunk is popcount(mask[e] &
+// lanes_below), and per-expert chunk counts are scanned across chunks.
+#pragma once
+
+#include "device_common.h"
+#include "dispatch_kernels.h"
+
+namespace moe {
+
+constexpr int kLlFusedMaxTokens = 1024;  // one block of up to 16 waves does the whole layout
+constexpr int kLlFusedMaxExperts = 512;  // 16 masks of E x 8 bytes fit in 64 KB of LDS
+
+struct LlLayoutArgs {
+  const int32_t* topk_idx;
+  int32_t* slot_local;  // plan: [T, k] position inside the token's chunk, or -1
+  int32_t* chunk_base;  // plan: [E, NC] chunk counts, then exclusive prefix per expert
+  int32_t* recv_count;  // out: [E]
+  int T, k, E, NC;
+};
+
+// Builds this wave's expert masks for its 64 tokens and writes in-chunk slot
+// positions.  `mask` is this wave's [E] array in LDS, already zeroed.
+__device__ __forceinline__ void ll_chunk_positions(const LlLayoutArgs& a, int chunk, int lane,
+                                                   unsigned long long* mask) {
+  const int t = chunk * kWave + lane;
+  const unsigned long long bit = 1ull << lane;
+  if (t < a.T) {
+    const int32_t* row = a.topk_idx + (size_t)t * a.k;
+    for (int j = 0; j < a.k; ++j) {
+      const int e = row[j];
+      if ((unsigned)e < (unsigned)a.E) atomicOr(&mask[e], bit);
+    }
+  }
+  __syncthreads();
+  if (t < a.T) {
+    const unsigned long long below = bit - 1ull;
+    const int32_t* row = a.topk_idx + (size_t)t * a.k;
+    for (int j = 0; j < a.k; ++j) {
+      const int e = row[j];
+      a.slot_local[(size_t)t * a.k + j] =
+          (unsigned)e < (unsigned)a.E ? __popcll(mask[e] & below) : -1;
+    }
+  }
+}
+
+// Multi-block pass 1: one 64-token chunk per block (one wave).  Dynamic LDS: E x u64.
+__global__ __launch_bounds__(kWave) void ll_count_kernel(LlLayoutArgs a) {
+  extern __shared__ unsigned long long mask[];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < a.E; e += kWave) mask[e] = 0ull;
+  __syncthreads();
+  ll_chunk_positions(a, blockIdx.x, lane, mask);
+  for (int e = lane; e < a.E; e += kWave) a.chunk_base[(size_t)e * a.NC + blockIdx.x] = __popcll(mask[e]);
+}
+
+// Multi-block pass 2: one wave per expert scans its chunk counts.
+__global__ __launch_bounds__(256) void ll_scan_kernel(LlLayoutArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= a.E) return;
+  int* row = a.chunk_base + (size_t)e * a.NC;
+  int carry = 0;
+  for (int c0 = 0; c0 < a.NC; c0 += kWave) {
+    const int c = c0 + lane;
+    const int v = c < a.NC ? row[c] : 0;
+    const int incl = wave_inclusive_scan(v, lane);
+    if (c < a.NC) row[c] = carry + incl - v;
+    carry += __shfl(incl, kWave - 1, kWave);
+  }
+  if (lane == 0) a.recv_count[e] = carry;
+}
+
+// T <= 1024 and E <= 512: one block, wave w owns chunk w.  Dynamic LDS: waves x E x u64.
+__global__ __launch_bounds__(kLlFusedMaxTokens) void ll_layout_fused_kernel(LlLayoutArgs a) {
+  extern __shared__ unsigned long long masks[];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+  for (int i = tid; i < nwaves * a.E; i += blockDim.x) masks[i] = 0ull;
+  __syncthreads();
+  ll_chunk_positions(a, wave, lane, masks + (size_t)wave * a.E);
+  __syncthreads();
+  for (int e = tid; e < a.E; e += blockDim.x) {  // serial scan over at most 16 chunks
+    int run = 0;
+    for (int c = 0; c < a.NC; ++c) {
+      a.chunk_base[(size_t)e * a.NC + c] = run;
+      run += __popcll(masks[(size_t)c * a.E + e]);
+    }
+    a.recv_count[e] = run;
+  }
+}
+
+struct LlDispatchArgs {
+  const uint16_t* x;
+  const int32_t* topk_idx;
+  const int32_t* slot_local;
+  const int32_t* chunk_base;
+  void* recv_x;         // [E, cap, H]
+  float* recv_scales;   // [E, cap, H/128]
+  int32_t* recv_src_idx;  // [E, cap]
+  int32_t* slot_pos;      // [T, k]
+  int T, H, H8, k, E, NC, cap;
+  int slices, items;
+};
+
+template <int U, bool kFp8>
+__global__ __launch_bounds__(kDispatchBlock) void ll_dispatch_kernel(LlDispatchArgs a) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x * (kDispatchBlock / kWave) + wave;
+  if (item >= a.items) return;
+  const int t = item / a.slices;
+  const int s = item - t * a.slices;
+  const int chunk = t >> 6;
+
+  // lane j < k: slot j's expert, receive position, and whether it is the first slot naming it
+  int e = -1, pos = -1;
+  if (lane < a.k) {
+    e = a.topk_idx[(size_t)t * a.k + lane];
+    if ((unsigned)e < (unsigned)a.E) {
+      pos = a.chunk_base[(size_t)e * a.NC + chunk] + a.slot_local[(size_t)t * a.k + lane];
+      if ((unsigned)pos >= (unsigned)a.cap) pos = -1;  // only a plan from another layout gets here
+    }
+  }
+  bool first = pos >= 0;
+  for (int j = 0; j < a.k; ++j) {  // an earlier slot naming the same expert sends the row
+    const int other = __shfl(e, j, kWave);
+    first = first && !(j < lane && other == e);
+  }
+
+  const int c0 = s * (U * kWave) + lane;
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H);
+  u32x4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = c0 + u * kWave;
+    v[u] = c < a.H8 ? __builtin_nontemporal_load(xrow + c) : u32x4{0u, 0u, 0u, 0u};
+  }
+  u32x2 q[U];
+  float sc[U];
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      sc[u] = fmaxf(block_amax(v[u]), kAmaxFloor) / kE4m3Max;
+      q[u] = quantize8(v[u], sc[u]);
+    }
+  }
+
+  if (s == 0 && lane < a.k) a.slot_pos[(size_t)t * a.k + lane] = pos;
+  uint64_t todo = __ballot(first);
+  while (todo) {
+    const int j = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    const int pj = __builtin_amdgcn_readlane(pos, j);
+    const size_t row = (size_t)ej * a.cap + pj;
+    if (s == 0 && lane == 0) a.recv_src_idx[row] = t;
+    if constexpr (kFp8) {
+      u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.recv_x) + row * a.H);
+      float* sdst = a.recv_scales + row * (a.H / kFp8Block);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * kWave;
+        if (c < a.H8) {
+          __builtin_nontemporal_store(q[u], dst + c);
+          if ((lane & 15) == 0) sdst[c >> 4] = sc[u];
+        }
+      }
+    } else {
+      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.recv_x) + row * a.H);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * kWave;
+        if (c < a.H8) __builtin_nontemporal_store(v[u], dst + c);
+      }
+    }
+  }
+}
+
+}  // namespace moe

@@ -16,6 +16,7 @@
 #include "device_common.h"
 #include "dispatch_kernels.h"
 #include "layout_kernels.h"
+#include "ll_kernels.h"
 
 namespace {
 
@@ -107,12 +108,6 @@ void launch_dispatch(int U, dim3 grid, hipStream_t stream, const moe::DispatchAr
   }
 }
 
-#ifndef MOE_COMBINE_PERSISTENT
-#define MOE_COMBINE_PERSISTENT 1
-#endif
-#ifndef MOE_COMBINE_PIPELINED
-#define MOE_COMBINE_PIPELINED 1
-#endif
 // Resident combine waves per CU in the persistent launch (2 per SIMD, each
 // with two items' payload in flight).
 #ifndef MOE_COMBINE_WAVES_PER_CU
@@ -132,25 +127,61 @@ int device_cu_count() {
   return cus;
 }
 
-void launch_combine(int U, dim3 grid, hipStream_t stream, const moe::CombineArgs& a) {
-  const dim3 block(moe::kCombineBlock);
-  if (MOE_COMBINE_PERSISTENT) {
-    const long waves = (long)device_cu_count() * MOE_COMBINE_WAVES_PER_CU;
-    const dim3 pgrid((unsigned)std::min<long>(grid.x, waves / (moe::kCombineBlock / moe::kWave)));
-    if (MOE_COMBINE_PIPELINED && a.k <= moe::kSlotBatch && a.num_y_rows >= 1) {
-      hipLaunchKernelGGL((moe::combine_pipelined_kernel<1>), pgrid, block, 0, stream, a);
-      return;
-    }
-    switch (U) {
-      case 2: hipLaunchKernelGGL((moe::combine_persistent_kernel<2>), pgrid, block, 0, stream, a); break;
-      default: hipLaunchKernelGGL((moe::combine_persistent_kernel<1>), pgrid, block, 0, stream, a); break;
-    }
-    return;
+__global__ __launch_bounds__(256) void zero_fill_kernel(moe::u32x4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = moe::u32x4{0u, 0u, 0u, 0u};
+}
+
+// Combine over T tokens: one wave per (token, 512-channel slice) item, on a
+// persistent grid.  With no rows of y every slot is skipped and out is +0.
+template <bool kPerExpert>
+moe_status launch_combine(moe::CombineArgs& a, void* out, hipStream_t stream) {
+  const size_t out16 = (size_t)a.T * a.H8;
+  if (a.num_y_rows == 0) {
+    const unsigned blocks = (unsigned)std::min<size_t>((out16 + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<moe::u32x4*>(out), out16);
+    return last_launch_status();
   }
+  a.slices = (a.H8 + moe::kWave - 1) / moe::kWave;
+  if ((int64_t)a.T * a.slices > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  a.items = a.T * a.slices;
+  const int waves_per_block = moe::kCombineBlock / moe::kWave;
+  const long resident = (long)device_cu_count() * MOE_COMBINE_WAVES_PER_CU / waves_per_block;
+  const dim3 grid((unsigned)std::min<long>((a.items + waves_per_block - 1) / waves_per_block, resident));
+  const dim3 block(moe::kCombineBlock);
+  if (a.k <= moe::kSlotBatch)
+    hipLaunchKernelGGL((moe::combine_pipelined_kernel<kPerExpert>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((moe::combine_persistent_kernel<kPerExpert>), grid, block, 0, stream, a);
+  return last_launch_status();
+}
+
+struct LlPlanLayout {
+  size_t slot_local, chunk_base, total;
+  int NC;
+};
+
+LlPlanLayout ll_plan_layout(const moe_shape& s) {
+  LlPlanLayout p{};
+  p.NC = (s.num_tokens + moe::kWave - 1) / moe::kWave;
+  size_t off = 0;
+  p.slot_local = off;
+  off = align_up(off + (size_t)s.num_tokens * s.num_topk * sizeof(int32_t), kPlanAlign);
+  p.chunk_base = off;
+  off = align_up(off + (size_t)s.num_experts * p.NC * sizeof(int32_t), kPlanAlign);
+  p.total = std::max(off, kPlanAlign);  // never empty: callers always pass a real allocation
+  return p;
+}
+
+template <bool kFp8>
+void launch_ll_dispatch(int U, dim3 grid, hipStream_t stream, const moe::LlDispatchArgs& a) {
+  const dim3 block(moe::kDispatchBlock);
   switch (U) {
-    case 4: hipLaunchKernelGGL((moe::combine_kernel<4>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((moe::combine_kernel<2>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((moe::combine_kernel<1>), grid, block, 0, stream, a); break;
+    case 14: hipLaunchKernelGGL((moe::ll_dispatch_kernel<14, kFp8>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((moe::ll_dispatch_kernel<7, kFp8>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((moe::ll_dispatch_kernel<4, kFp8>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((moe::ll_dispatch_kernel<2, kFp8>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((moe::ll_dispatch_kernel<1, kFp8>), grid, block, 0, stream, a); break;
   }
 }
 
@@ -330,19 +361,121 @@ moe_status moe_combine(const moe_shape* shape, const void* y, int32_t num_y_rows
   a.E = s.num_experts;
   a.R = s.num_ranks;
   a.num_y_rows = num_y_rows;
-#ifdef MOE_FORCE_COMBINE_U
-  const int U = MOE_FORCE_COMBINE_U;
-#else
-  const int U = 1;
-#endif
+  return launch_combine<false>(a, out, stream);
+}
+
+size_t moe_ll_workspace_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return ll_plan_layout(*shape).total;
+}
+
+moe_status moe_dispatch_ll(const moe_shape* shape, moe_dtype dtype, const void* x, const int32_t* topk_idx,
+                           void* workspace, size_t workspace_bytes, int32_t expert_capacity, void* recv_x,
+                           float* recv_scales, int32_t* recv_src_idx, int32_t* recv_count, int32_t* slot_pos,
+                           hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape s = *shape;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = dtype == MOE_FP8_E4M3;
+  if (fp8 && s.hidden % moe::kFp8Block != 0) return MOE_ERR_INVALID_ARG;
+  if (expert_capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (expert_capacity < s.num_tokens) return MOE_ERR_CAPACITY;
+  const int64_t T = s.num_tokens, rows = (int64_t)s.num_experts * expert_capacity;
+  if (rows > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!present(x, T) || !present(topk_idx, T) || !present(slot_pos, T) || !workspace || !recv_count ||
+      !present(recv_x, rows) || !present(recv_src_idx, rows) || (fp8 && !present(recv_scales, rows)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 4) || !aligned(workspace, kPlanAlign) ||
+      !aligned(recv_src_idx, 4) || !aligned(recv_count, 4) || !aligned(slot_pos, 4) ||
+      (fp8 && !aligned(recv_scales, 4)))
+    return MOE_ERR_INVALID_ARG;
+  const LlPlanLayout p = ll_plan_layout(s);
+  if (workspace_bytes < p.total) return MOE_ERR_INVALID_ARG;
+
+  char* ws = static_cast<char*>(workspace);
+  moe::LlLayoutArgs la{};
+  la.topk_idx = topk_idx;
+  la.slot_local = reinterpret_cast<int32_t*>(ws + p.slot_local);
+  la.chunk_base = reinterpret_cast<int32_t*>(ws + p.chunk_base);
+  la.recv_count = recv_count;
+  la.T = s.num_tokens;
+  la.k = s.num_topk;
+  la.E = s.num_experts;
+  la.NC = p.NC;
+  const int nwaves = std::max(1, p.NC);
+  const size_t fused_lds = (size_t)nwaves * s.num_experts * sizeof(unsigned long long);
+  if (s.num_tokens <= moe::kLlFusedMaxTokens && fused_lds <= 64 * 1024) {
+    hipLaunchKernelGGL(moe::ll_layout_fused_kernel, dim3(1), dim3(nwaves * moe::kWave), fused_lds, stream, la);
+  } else {
+    hipLaunchKernelGGL(moe::ll_count_kernel, dim3(p.NC), dim3(moe::kWave),
+                       (size_t)s.num_experts * sizeof(unsigned long long), stream, la);
+    hipLaunchKernelGGL(moe::ll_scan_kernel, dim3((s.num_experts + 3) / 4), dim3(256), 0, stream, la);
+  }
+  st = last_launch_status();
+  if (st != MOE_OK || s.num_tokens == 0) return st;
+
+  moe::LlDispatchArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.topk_idx = topk_idx;
+  a.slot_local = la.slot_local;
+  a.chunk_base = la.chunk_base;
+  a.recv_x = recv_x;
+  a.recv_scales = recv_scales;
+  a.recv_src_idx = recv_src_idx;
+  a.slot_pos = slot_pos;
+  a.T = s.num_tokens;
+  a.H = s.hidden;
+  a.H8 = s.hidden / 8;
+  a.k = s.num_topk;
+  a.E = s.num_experts;
+  a.NC = p.NC;
+  a.cap = expert_capacity;
+  const int U = pick_dispatch_chunks_per_lane(s.num_tokens, a.H8, fp8);
   const int groups = (a.H8 + moe::kWave - 1) / moe::kWave;
   a.slices = (groups + U - 1) / U;
   if ((int64_t)s.num_tokens * a.slices > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   a.items = s.num_tokens * a.slices;
-  const int waves_per_block = moe::kCombineBlock / moe::kWave;
+  const int waves_per_block = moe::kDispatchBlock / moe::kWave;
   const dim3 grid((a.items + waves_per_block - 1) / waves_per_block);
-  launch_combine(U, grid, stream, a);
+  if (fp8)
+    launch_ll_dispatch<true>(U, grid, stream, a);
+  else
+    launch_ll_dispatch<false>(U, grid, stream, a);
   return last_launch_status();
+}
+
+moe_status moe_combine_ll(const moe_shape* shape, const void* y, int32_t expert_capacity, const int32_t* topk_idx,
+                          const float* topk_w, const int32_t* slot_pos, void* out, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape s = *shape;
+  if (expert_capacity < 0) return MOE_ERR_INVALID_ARG;
+  const int64_t T = s.num_tokens, rows = (int64_t)s.num_experts * expert_capacity;
+  if (rows > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!present(y, rows) || !present(topk_idx, T) || !present(topk_w, T) || !present(slot_pos, T) ||
+      !present(out, T))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
+      !aligned(slot_pos, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (s.num_tokens == 0) return MOE_OK;
+
+  moe::CombineArgs a{};
+  a.y = static_cast<const uint16_t*>(y);
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.slot_pos = slot_pos;
+  a.out = static_cast<uint16_t*>(out);
+  a.T = s.num_tokens;
+  a.H = s.hidden;
+  a.H8 = s.hidden / 8;
+  a.k = s.num_topk;
+  a.E = s.num_experts;
+  a.R = s.num_ranks;
+  a.cap = expert_capacity;
+  a.num_y_rows = (int)rows;
+  return launch_combine<true>(a, out, stream);
 }
 
 }  // extern "C"

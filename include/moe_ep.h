@@ -161,6 +161,53 @@ moe_status moe_combine(const moe_shape* shape, const void* y, int32_t num_y_rows
                        const int32_t* topk_idx, const float* topk_w, const int32_t* send_row,
                        void* out, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Low-latency (per-expert) layout.  [DeepEP overview: the low-latency kernels
+ * for decoding; overlap notes, 节点间通信: the low-latency mode.]  The receive
+ * side keeps one fixed-capacity buffer per expert: buffers are [E, cap, ...],
+ * i.e. R ranks x [L, cap, ...] as each rank would hold its local experts.
+ * One receive row per (token, distinct valid expert); token t's row in expert
+ * e's buffer is pos(t, e) = number of tokens t' < t naming e.  The layout is
+ * computed inside moe_dispatch_ll (no separate layout call).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace moe_dispatch_ll needs for `shape` (0 if invalid). */
+size_t moe_ll_workspace_bytes(const moe_shape* shape);
+
+/* Low-latency dispatch.
+ *
+ *   dtype            MOE_BF16 or MOE_FP8_E4M3 (same per-128 scaling as moe_dispatch)
+ *   x                in  bf16[T, H]
+ *   topk_idx         in  int32[T, k]
+ *   workspace        scratch, >= moe_ll_workspace_bytes(shape) bytes, 256-byte aligned
+ *   expert_capacity      rows per expert buffer; >= T (else MOE_ERR_CAPACITY)
+ *   recv_x           out bf16 or uint8 [E, cap, H]
+ *   recv_scales      out float[E, cap, H/128] (FP8 only; NULL allowed for MOE_BF16)
+ *   recv_src_idx     out int32[E, cap]   source token of each written row
+ *   recv_count       out int32[E]        rows written per expert (distinct tokens naming it)
+ *   slot_pos         out int32[T, k]     pos(t, e_tj) for valid slots (shared by repeated
+ *                                        ids of one token), else -1: the combine handle
+ *
+ * Rows at or beyond recv_count[e] are not written.
+ */
+moe_status moe_dispatch_ll(const moe_shape* shape, moe_dtype dtype, const void* x, const int32_t* topk_idx,
+                           void* workspace, size_t workspace_bytes, int32_t expert_capacity, void* recv_x,
+                           float* recv_scales, int32_t* recv_src_idx, int32_t* recv_count,
+                           int32_t* slot_pos, hipStream_t stream);
+
+/* Low-latency combine: out[t] = BF16_RNE(sum over valid slots j, ascending, in fp32 without
+ * fused multiply-add, of topk_w[t, j] * y[e_tj, slot_pos[t, j]]).
+ *
+ *   y                in  bf16[E, cap, H]  expert outputs in the per-expert layout
+ *   expert_capacity      cap of y
+ *   topk_idx, topk_w in  int32/float[T, k]
+ *   slot_pos         in  int32[T, k]      from moe_dispatch_ll
+ *   out              out bf16[T, H]
+ */
+moe_status moe_combine_ll(const moe_shape* shape, const void* y, int32_t expert_capacity,
+                          const int32_t* topk_idx, const float* topk_w, const int32_t* slot_pos,
+                          void* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

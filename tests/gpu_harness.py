@@ -76,3 +76,36 @@ def run_combine(shape, y: np.ndarray, idx_d: torch.Tensor, w_d: torch.Tensor, se
     moe.moe_combine(shape, yd, idx_d, w_d, send_row_d, out, num_y_rows=num_y_rows)
     torch.cuda.synchronize()
     return bf16_to_np(out)
+
+
+def run_dispatch_ll(x: np.ndarray, topk_idx: np.ndarray, E: int, cap: int, dtype: str) -> PathResult:
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    shape = moe.MoeShape(T, H, k, E, 1)
+    xd = to_dev_bf16(x) if T else torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    idx_d = torch.from_numpy(np.ascontiguousarray(topk_idx, dtype=np.int32)).cuda()
+    d = moe.alloc_dispatch_ll(shape, dtype, capacity=cap)
+    _poison({k_: v for k_, v in d.items() if k_ != "workspace"})
+    moe.run_dispatch_ll(shape, dtype, xd, idx_d, d)
+    torch.cuda.synchronize()
+    r = PathResult()
+    r["shape"] = shape
+    for key in ("recv_src_idx", "recv_count", "slot_pos"):
+        r[key] = d[key].cpu().numpy()
+    r["recv_x"] = bf16_to_np(d["recv_x"]) if dtype == "bf16" else d["recv_x"].cpu().numpy()
+    if dtype == "fp8":
+        r["recv_scales"] = d["recv_scales"].cpu().numpy()
+    r["_dev"] = {"x": xd, "idx": idx_d, "d": d}
+    return r
+
+
+def run_combine_ll(shape, y: np.ndarray, idx_d: torch.Tensor, w: np.ndarray, slot_pos_d: torch.Tensor) -> np.ndarray:
+    E, cap, H = y.shape
+    yd = to_dev_bf16(y.reshape(E * cap, H)).view(E, cap, H) if y.size else \
+        torch.empty((E, cap, H), dtype=torch.bfloat16, device="cuda")
+    w_d = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).cuda()
+    out = torch.empty((shape.num_tokens, H), dtype=torch.bfloat16, device="cuda")
+    out.view(torch.uint8).fill_(POISON)
+    moe.moe_combine_ll(shape, yd, idx_d, w_d, slot_pos_d, out)
+    torch.cuda.synchronize()
+    return bf16_to_np(out)

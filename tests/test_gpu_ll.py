@@ -1,0 +1,119 @@
+"""GPU parity of the low-latency (per-expert) layout: moe_dispatch_ll / moe_combine_ll against the oracle.
+
+Bar: recv_count, slot_pos, recv_src_idx, bf16 rows, FP8 bytes and scales bit-exact; rows at or
+beyond recv_count[e] untouched; combine within 1 bf16 ulp and expected bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import moe_oracle as O
+from tests.checks import within_one_bf16_ulp
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def G():
+    from tests import gpu_harness
+    return gpu_harness
+
+
+def ll_y(count, cap, H, seed):
+    """Expert outputs in the per-expert layout: random rows where tokens were received, zeros elsewhere."""
+    E = count.size
+    y = np.zeros((E, cap, H), np.uint16)
+    rows = W.draw_expert_outputs(np.random.default_rng(seed), int(count.sum()), H)
+    i = 0
+    for e in range(E):
+        y[e, :count[e]] = rows[i:i + count[e]]
+        i += count[e]
+    return y
+
+
+def run_ll_case(x, idx, w, E, cap, dtype, seed=0, sample=None):
+    print(f"[case] ll T={x.shape[0]} H={x.shape[1]} E={E} k={idx.shape[1]} cap={cap} {dtype}", flush=True)
+    res = G().run_dispatch_ll(x, idx, E, cap, dtype)
+    count, slot_pos = O.ll_layout(idx, E)
+    assert np.array_equal(res["recv_count"], count)
+    assert np.array_equal(res["slot_pos"], slot_pos)
+    src = res["recv_src_idx"]
+    for e in range(E):
+        n = count[e]
+        tok = np.nonzero((idx == e).any(axis=1))[0]
+        assert np.array_equal(src[e, :n], tok), e
+        assert (src[e, n:].view(np.uint32) == 0x7B7B7B7B).all()
+        assert (res["recv_x"][e, n:].view(np.uint8) == 0x7B).all()
+    toks = np.arange(x.shape[0]) if sample is None else sample
+    if dtype == "bf16":
+        ee, pp = np.nonzero(np.arange(cap)[None, :] < count[:, None])
+        sel = np.isin(src[ee, pp], toks)
+        assert np.array_equal(res["recv_x"][ee[sel], pp[sel]], x[src[ee[sel], pp[sel]]])
+    else:
+        q, s = O.quantize_fp8_blocks(x[toks])
+        where = {int(t): i for i, t in enumerate(toks)}
+        for e in range(E):
+            for p in range(count[e]):
+                t = int(src[e, p])
+                if t in where:
+                    assert np.array_equal(res["recv_x"][e, p], q[where[t]]), (e, p)
+                    assert np.array_equal(res["recv_scales"][e, p].view(np.uint32), s[where[t]].view(np.uint32))
+    y = ll_y(count, cap, x.shape[1], seed)
+    dev = res["_dev"]
+    out = G().run_combine_ll(res["shape"], y, dev["idx"], w, dev["d"]["slot_pos"])
+    ref = O.ll_combine(y, idx, w, slot_pos, E)
+    assert within_one_bf16_ulp(out, ref).all()
+    assert np.array_equal(out, ref)
+    return res
+
+
+def test_ll_decode_workload():
+    cfg = W.CONFIG_BY_NAME["decode"]
+    d = W.make_inputs(cfg)
+    run_ll_case(d["x"], d["topk_idx"], d["topk_w"], cfg.num_experts, cfg.num_tokens, "fp8", seed=1)
+
+
+@pytest.mark.parametrize("case", [
+    # name, seed, T, H, E, k, dtype, invalid_frac, capacity extra
+    ("small_bf16", 1, 37, 256, 16, 4, "bf16", 0.2, 5),
+    ("one_token", 2, 1, 128, 8, 2, "fp8", 0.0, 0),
+    ("multiblock", 3, 1100, 256, 64, 6, "bf16", 0.1, 0),
+    ("many_experts", 4, 200, 128, 4096, 32, "fp8", 0.1, 0),
+    ("fused_wide", 5, 1024, 128, 512, 8, "fp8", 0.0, 0),
+    ("ragged_hidden", 6, 300, 136, 32, 4, "bf16", 0.0, 3),
+])
+def test_ll_edges(case):
+    name, seed, T, H, E, k, dtype, inv, extra = case
+    d = W.random_case(seed, T, H, E, k, 1, invalid_frac=inv)
+    idx = d["topk_idx"].copy()
+    if T > 3:
+        idx[2, :2] = max(int(idx[2, 0]), 0)  # one token names an expert twice
+    run_ll_case(d["x"], idx, d["topk_w"], E, T + extra, dtype, seed=seed)
+
+
+def test_ll_empty_and_capacity_error():
+    import combine_get_dispatch_07_amd as moe
+    res = G().run_dispatch_ll(np.zeros((0, 256), np.uint16), np.zeros((0, 4), np.int32), 16, 0, "bf16")
+    assert (res["recv_count"] == 0).all()
+    x = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda")
+    idx = torch.zeros((8, 4), dtype=torch.int32, device="cuda")
+    shape = moe.MoeShape(8, 256, 4, 16, 1)
+    d = moe.alloc_dispatch_ll(shape, "bf16", capacity=7)
+    with pytest.raises(moe.MoeError) as e:
+        moe.run_dispatch_ll(shape, "bf16", x, idx, d)
+    assert e.value.code == 2
+
+
+def test_combine_with_no_expert_rows_is_zero():
+    d = W.random_case(9, 50, 256, 16, 4, 4)
+    from tests import gpu_harness as H
+    res = H.run_layout_dispatch(d["x"], d["topk_idx"], d["topk_w"], 16, 4, "bf16")
+    out = H.run_combine(res["shape"], np.zeros((0, 256), np.uint16), res["_dev"]["idx"], res["_dev"]["w"],
+                        res["_dev"]["d"]["send_row"], num_y_rows=0)
+    assert (out == 0).all()
