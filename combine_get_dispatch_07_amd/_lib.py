@@ -76,6 +76,10 @@ def _load() -> ctypes.CDLL:
     lib.moe_dispatch_ll.restype = ctypes.c_int
     lib.moe_combine_ll.argtypes = [SH, P, I32, P, P, P, P, P]
     lib.moe_combine_ll.restype = ctypes.c_int
+    lib.moe_combine_backward.argtypes = [SH, P, P, I32, P, P, P, P, P, P]
+    lib.moe_combine_backward.restype = ctypes.c_int
+    lib.moe_dispatch_backward.argtypes = [SH, P, I32, P, P, P, P, P, P]
+    lib.moe_dispatch_backward.restype = ctypes.c_int
     return lib
 
 
@@ -190,3 +194,29 @@ def moe_combine_ll(shape: MoeShape, y, topk_idx, topk_w, slot_pos, out, stream=N
         _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
         _ptr(slot_pos, "slot_pos", torch.int32, T * k), _ptr(out, "out", torch.bfloat16, T * H), _stream(stream))
     _check("moe_combine_ll", code)
+
+
+def moe_combine_backward(shape: MoeShape, grad_out, y, topk_idx, topk_w, send_row, grad_y, grad_topk_w,
+                         stream=None, num_y_rows=None) -> None:
+    T, H, k, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
+    rows = y.shape[0] if num_y_rows is None else int(num_y_rows)
+    code = lib.moe_combine_backward(
+        ctypes.byref(shape.c()), _ptr(grad_out, "grad_out", torch.bfloat16, T * H),
+        _ptr(y, "y", torch.bfloat16, rows * H), rows, _ptr(topk_idx, "topk_idx", torch.int32, T * k),
+        _ptr(topk_w, "topk_w", torch.float32, T * k), _ptr(send_row, "send_row", torch.int32, T * R),
+        _ptr(grad_y, "grad_y", torch.bfloat16, rows * H), _ptr(grad_topk_w, "grad_topk_w", torch.float32, T * k),
+        _stream(stream))
+    _check("moe_combine_backward", code)
+
+
+def moe_dispatch_backward(shape: MoeShape, grad_recv_x, topk_idx, send_row, grad_x, grad_recv_topk_w=None,
+                          grad_topk_w=None, stream=None, num_recv_rows=None) -> None:
+    T, H, k, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
+    rows = grad_recv_x.shape[0] if num_recv_rows is None else int(num_recv_rows)
+    code = lib.moe_dispatch_backward(
+        ctypes.byref(shape.c()), _ptr(grad_recv_x, "grad_recv_x", torch.bfloat16, rows * H), rows,
+        _ptr(grad_recv_topk_w, "grad_recv_topk_w", torch.float32, rows * k),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(send_row, "send_row", torch.int32, T * R),
+        _ptr(grad_x, "grad_x", torch.bfloat16, T * H), _ptr(grad_topk_w, "grad_topk_w", torch.float32, T * k),
+        _stream(stream))
+    _check("moe_dispatch_backward", code)

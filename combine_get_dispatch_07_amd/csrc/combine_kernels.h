@@ -7,7 +7,9 @@
 // Per token and channel: acc = +0; for j = 0..k-1 over valid slots,
 // acc = fl32(acc + fl32(w_j * y[row(t, j)])); out = bf16_rne(acc).
 // row(t, j) is send_row[t, rank(e_j)] for the rank layout, or
-// e_j * cap + slot_pos[t, j] for the per-expert (low-latency) layout.
+// e_j * cap + slot_pos[t, j] for the per-expert (low-latency) layout.  The
+// same gather with weight 1 over the token's distinct rank rows (j = rank,
+// ascending) is the dispatch backward: grad_x[t] = sum_r grad_recv[send_row[t, r]].
 //
 // A gather, not a scatter: each (token, 512-channel slice) is owned by one
 // wave, so there are no float atomics and the summation order is fixed.  A
@@ -29,6 +31,13 @@ namespace moe {
 constexpr int kCombineBlock = 256;
 constexpr int kSlotBatch = 8;
 
+// How term j of token t finds its row of y and its weight.
+enum RowMode : int {
+  kRankSlots = 0,    // j = slot: row send_row[t, rank(e_j)], weight topk_w[t, j]
+  kExpertSlots = 1,  // j = slot: row e_j * cap + slot_pos[t, j], weight topk_w[t, j]
+  kRankRows = 2,     // j = rank: row send_row[t, j], weight 1
+};
+
 struct CombineArgs {
   const uint16_t* y;
   const int32_t* topk_idx;
@@ -40,6 +49,7 @@ struct CombineArgs {
   int T, H, H8, k, E, R;
   int cap;         // per-expert layout: rows per expert
   int num_y_rows;  // rows of y; slots whose row falls outside are skipped
+  int terms;       // terms per token: k, or R for kRankRows
   int slices;
   int items;
 };
@@ -50,28 +60,38 @@ struct RawMeta {
 };
 
 // Unconditional loads from clamped, always valid addresses (masked in resolve_row).
-template <bool kPerExpert>
+template <int kMode>
 __device__ __forceinline__ RawMeta load_raw_meta(const CombineArgs& a, int item, int lane) {
   const int t = min(item, a.items - 1) / a.slices;
-  const int j = min(lane, a.k - 1);
   RawMeta m;
-  m.id = a.topk_idx[(size_t)t * a.k + j];
-  m.w = a.topk_w[(size_t)t * a.k + j];
-  if constexpr (kPerExpert)
-    m.rr = a.slot_pos[(size_t)t * a.k + j];
-  else
+  if constexpr (kMode == kRankRows) {
+    m.id = 0;
+    m.w = 1.0f;
     m.rr = a.send_row[(size_t)t * a.R + min(lane, a.R - 1)];
+  } else {
+    const int j = min(lane, a.k - 1);
+    m.id = a.topk_idx[(size_t)t * a.k + j];
+    m.w = a.topk_w[(size_t)t * a.k + j];
+    if constexpr (kMode == kExpertSlots)
+      m.rr = a.slot_pos[(size_t)t * a.k + j];
+    else
+      m.rr = a.send_row[(size_t)t * a.R + min(lane, a.R - 1)];
+  }
   return m;
 }
 
-// Lane j: the y row of slot j, or -1.
-template <bool kPerExpert>
+// Lane j: the y row of term j, or -1.
+template <int kMode>
 __device__ __forceinline__ int resolve_row(const CombineArgs& a, const RawMeta& m, int item, int lane) {
-  const bool valid = item < a.items && lane < a.k && (unsigned)m.id < (unsigned)a.E;
+  bool valid = item < a.items && lane < a.terms;
   int row;
-  if constexpr (kPerExpert) {
+  if constexpr (kMode == kRankRows) {
+    row = m.rr;
+  } else if constexpr (kMode == kExpertSlots) {
+    valid = valid && (unsigned)m.id < (unsigned)a.E;
     row = valid && m.rr >= 0 && m.rr < a.cap ? m.id * a.cap + m.rr : -1;
   } else {
+    valid = valid && (unsigned)m.id < (unsigned)a.E;
     row = __shfl(m.rr, valid ? rank_of(m.id, a.rank_magic) : 0, kWave);
   }
   return valid && (unsigned)row < (unsigned)a.num_y_rows ? row : -1;
@@ -100,7 +120,7 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], float w, const u32x4
 }
 
 // ---------------------------------------------------------------------------
-// k <= 8: two-deep software pipeline.  Vector loads retire in order against
+// terms <= 8: two-deep software pipeline.  Vector loads retire in order against
 // one counter, so per item i the loop issues, in this order: (1) the metadata
 // of item i+2, (2) the payload of item i+1; then it waits only for item i's
 // payload (accumulate, store) and for item i+2's metadata (resolve its rows),
@@ -113,9 +133,9 @@ struct SlotRows {
   float w[kSlotBatch];
 };
 
-template <bool kPerExpert>
+template <int kMode>
 __device__ __forceinline__ SlotRows resolve_rows(const CombineArgs& a, const RawMeta& m, int item, int lane) {
-  const int row = resolve_row<kPerExpert>(a, m, item, lane);
+  const int row = resolve_row<kMode>(a, m, item, lane);
   SlotRows r;
 #pragma unroll
   for (int j = 0; j < kSlotBatch; ++j) {
@@ -135,11 +155,11 @@ __device__ __forceinline__ void load_payload(const CombineArgs& a, const SlotRow
   }
 }
 
-template <bool kPerExpert>
+template <int kMode>
 __device__ __forceinline__ void combine_stage(const CombineArgs& a, int item, int nw, int lane, SlotRows& cur,
                                               SlotRows& nxt, const u32x4 (&pc)[kSlotBatch],
                                               u32x4 (&pn)[kSlotBatch]) {
-  const RawMeta m2 = load_raw_meta<kPerExpert>(a, item + 2 * nw, lane);
+  const RawMeta m2 = load_raw_meta<kMode>(a, item + 2 * nw, lane);
   load_payload(a, nxt, item + nw, lane, pn);
 
   const int t = item / a.slices;
@@ -152,10 +172,10 @@ __device__ __forceinline__ void combine_stage(const CombineArgs& a, int item, in
     if (cur.row[j] >= 0) accumulate(acc, cur.w[j], pc[j]);
   if (c < a.H8) store_out(reinterpret_cast<u32x4*>(a.out + (size_t)t * a.H), c, acc);
   cur = nxt;
-  nxt = resolve_rows<kPerExpert>(a, m2, item + 2 * nw, lane);
+  nxt = resolve_rows<kMode>(a, m2, item + 2 * nw, lane);
 }
 
-template <bool kPerExpert>
+template <int kMode>
 __global__ __launch_bounds__(kCombineBlock) void combine_pipelined_kernel(CombineArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -163,27 +183,27 @@ __global__ __launch_bounds__(kCombineBlock) void combine_pipelined_kernel(Combin
   int item = blockIdx.x * (kCombineBlock / kWave) + wave;
   if (item >= a.items) return;
 
-  const RawMeta m0 = load_raw_meta<kPerExpert>(a, item, lane);
-  const RawMeta m1 = load_raw_meta<kPerExpert>(a, item + nw, lane);
-  SlotRows cur = resolve_rows<kPerExpert>(a, m0, item, lane);
+  const RawMeta m0 = load_raw_meta<kMode>(a, item, lane);
+  const RawMeta m1 = load_raw_meta<kMode>(a, item + nw, lane);
+  SlotRows cur = resolve_rows<kMode>(a, m0, item, lane);
   u32x4 buf_a[kSlotBatch], buf_b[kSlotBatch];
   load_payload(a, cur, item, lane, buf_a);
-  SlotRows nxt = resolve_rows<kPerExpert>(a, m1, item + nw, lane);
+  SlotRows nxt = resolve_rows<kMode>(a, m1, item + nw, lane);
   for (;;) {
-    combine_stage<kPerExpert>(a, item, nw, lane, cur, nxt, buf_a, buf_b);
+    combine_stage<kMode>(a, item, nw, lane, cur, nxt, buf_a, buf_b);
     item += nw;
     if (item >= a.items) break;
-    combine_stage<kPerExpert>(a, item, nw, lane, cur, nxt, buf_b, buf_a);
+    combine_stage<kMode>(a, item, nw, lane, cur, nxt, buf_b, buf_a);
     item += nw;
     if (item >= a.items) break;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Any k (up to 32): persistent loop, slots in batches of 8 (rows of a batch
+// Any number of terms (up to 64): persistent loop, terms in batches of 8 (rows of a batch
 // are loaded before any is accumulated); the next item's metadata is fetched
 // behind the current payload.  Requires num_y_rows >= 1.
-template <bool kPerExpert>
+template <int kMode>
 __global__ __launch_bounds__(kCombineBlock) void combine_persistent_kernel(CombineArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -191,24 +211,24 @@ __global__ __launch_bounds__(kCombineBlock) void combine_persistent_kernel(Combi
   int item = blockIdx.x * (kCombineBlock / kWave) + wave;
   if (item >= a.items) return;
 
-  RawMeta m = load_raw_meta<kPerExpert>(a, item, lane);
+  RawMeta m = load_raw_meta<kMode>(a, item, lane);
   for (; item < a.items; item += nw) {
     const int t = item / a.slices;
     const int c = (item - t * a.slices) * kWave + lane;
     const int cc = min(c, a.H8 - 1);
-    const int slot_row = resolve_row<kPerExpert>(a, m, item, lane);
+    const int slot_row = resolve_row<kMode>(a, m, item, lane);
     const float slot_w = m.w;
-    m = load_raw_meta<kPerExpert>(a, item + nw, lane);  // next item's metadata, in flight meanwhile
+    m = load_raw_meta<kMode>(a, item + nw, lane);  // next item's metadata, in flight meanwhile
 
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int j0 = 0; j0 < a.k; j0 += kSlotBatch) {
+    for (int j0 = 0; j0 < a.terms; j0 += kSlotBatch) {
       int row[kSlotBatch];
       float w[kSlotBatch];
       u32x4 v[kSlotBatch];
 #pragma unroll
-      for (int jj = 0; jj < kSlotBatch; ++jj) {  // lanes >= k hold row -1
+      for (int jj = 0; jj < kSlotBatch; ++jj) {  // lanes >= terms hold row -1
         row[jj] = __builtin_amdgcn_readlane(slot_row, j0 + jj);
         w[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(slot_w), j0 + jj));
         v[jj] = reinterpret_cast<const u32x4*>(a.y + (size_t)max(row[jj], 0) * a.H)[cc];

@@ -12,6 +12,7 @@
 
 #include "moe_ep.h"
 
+#include "backward_kernels.h"
 #include "combine_kernels.h"
 #include "device_common.h"
 #include "dispatch_kernels.h"
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(moe::u32x4* p, size_t n1
 
 // Combine over T tokens: one wave per (token, 512-channel slice) item, on a
 // persistent grid.  With no rows of y every slot is skipped and out is +0.
-template <bool kPerExpert>
+template <int kMode>
 moe_status launch_combine(moe::CombineArgs& a, void* out, hipStream_t stream) {
   const size_t out16 = (size_t)a.T * a.H8;
   if (a.num_y_rows == 0) {
@@ -149,10 +150,11 @@ moe_status launch_combine(moe::CombineArgs& a, void* out, hipStream_t stream) {
   const long resident = (long)device_cu_count() * MOE_COMBINE_WAVES_PER_CU / waves_per_block;
   const dim3 grid((unsigned)std::min<long>((a.items + waves_per_block - 1) / waves_per_block, resident));
   const dim3 block(moe::kCombineBlock);
-  if (a.k <= moe::kSlotBatch)
-    hipLaunchKernelGGL((moe::combine_pipelined_kernel<kPerExpert>), grid, block, 0, stream, a);
+  a.terms = kMode == moe::kRankRows ? a.R : a.k;
+  if (a.terms <= moe::kSlotBatch)
+    hipLaunchKernelGGL((moe::combine_pipelined_kernel<kMode>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((moe::combine_persistent_kernel<kPerExpert>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe::combine_persistent_kernel<kMode>), grid, block, 0, stream, a);
   return last_launch_status();
 }
 
@@ -361,7 +363,7 @@ moe_status moe_combine(const moe_shape* shape, const void* y, int32_t num_y_rows
   a.E = s.num_experts;
   a.R = s.num_ranks;
   a.num_y_rows = num_y_rows;
-  return launch_combine<false>(a, out, stream);
+  return launch_combine<moe::kRankSlots>(a, out, stream);
 }
 
 size_t moe_ll_workspace_bytes(const moe_shape* shape) {
@@ -475,7 +477,95 @@ moe_status moe_combine_ll(const moe_shape* shape, const void* y, int32_t expert_
   a.R = s.num_ranks;
   a.cap = expert_capacity;
   a.num_y_rows = (int)rows;
-  return launch_combine<true>(a, out, stream);
+  return launch_combine<moe::kExpertSlots>(a, out, stream);
+}
+
+moe_status moe_combine_backward(const moe_shape* shape, const void* grad_out, const void* y, int32_t num_y_rows,
+                                const int32_t* topk_idx, const float* topk_w, const int32_t* send_row,
+                                void* grad_y, float* grad_topk_w, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape s = *shape;
+  if (num_y_rows < 0) return MOE_ERR_INVALID_ARG;
+  const int64_t T = s.num_tokens;
+  if (!present(grad_out, T) || !present(y, num_y_rows) || !present(topk_idx, T) || !present(topk_w, T) ||
+      !present(send_row, T) || !present(grad_y, num_y_rows) || !present(grad_topk_w, T))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(grad_out, 16) || !aligned(y, 16) || !aligned(grad_y, 16) || !aligned(topk_idx, 4) ||
+      !aligned(topk_w, 4) || !aligned(send_row, 4) || !aligned(grad_topk_w, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (s.num_tokens == 0) return MOE_OK;
+
+  moe::CombineBwdArgs a{};
+  a.g = static_cast<const uint16_t*>(grad_out);
+  a.y = static_cast<const uint16_t*>(y);
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.send_row = send_row;
+  a.grad_y = static_cast<uint16_t*>(grad_y);
+  a.grad_w = grad_topk_w;
+  a.rank_magic = rank_magic(s);
+  a.T = s.num_tokens;
+  a.H = s.hidden;
+  a.H8 = s.hidden / 8;
+  a.k = s.num_topk;
+  a.E = s.num_experts;
+  a.R = s.num_ranks;
+  a.num_y_rows = num_y_rows;
+  const dim3 grid(s.num_tokens), block(moe::kBwdWaves * moe::kWave);
+  if (s.num_topk <= 8)
+    hipLaunchKernelGGL(moe::combine_backward_kernel<8>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(moe::combine_backward_kernel<moe::kMaxTopk>, grid, block, 0, stream, a);
+  return last_launch_status();
+}
+
+moe_status moe_dispatch_backward(const moe_shape* shape, const void* grad_recv_x, int32_t num_recv_rows,
+                                 const float* grad_recv_topk_w, const int32_t* topk_idx, const int32_t* send_row,
+                                 void* grad_x, float* grad_topk_w, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape s = *shape;
+  if (num_recv_rows < 0) return MOE_ERR_INVALID_ARG;
+  if ((grad_recv_topk_w == nullptr) != (grad_topk_w == nullptr)) return MOE_ERR_INVALID_ARG;
+  const bool weights = grad_topk_w != nullptr;
+  const int64_t T = s.num_tokens;
+  if (!present(grad_recv_x, num_recv_rows) || !present(send_row, T) || !present(grad_x, T) ||
+      (weights && (!present(topk_idx, T) || !present(grad_recv_topk_w, num_recv_rows))))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(grad_recv_x, 16) || !aligned(grad_x, 16) || !aligned(send_row, 4) || !aligned(topk_idx, 4) ||
+      !aligned(grad_recv_topk_w, 4) || !aligned(grad_topk_w, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (s.num_tokens == 0) return MOE_OK;
+
+  moe::CombineArgs a{};
+  a.y = static_cast<const uint16_t*>(grad_recv_x);
+  a.send_row = send_row;
+  a.out = static_cast<uint16_t*>(grad_x);
+  a.T = s.num_tokens;
+  a.H = s.hidden;
+  a.H8 = s.hidden / 8;
+  a.k = s.num_topk;
+  a.E = s.num_experts;
+  a.R = s.num_ranks;
+  a.num_y_rows = num_recv_rows;
+  st = launch_combine<moe::kRankRows>(a, grad_x, stream);
+  if (st != MOE_OK || !weights) return st;
+
+  moe::WeightGradArgs wa{};
+  wa.grad_recv_w = grad_recv_topk_w;
+  wa.topk_idx = topk_idx;
+  wa.send_row = send_row;
+  wa.grad_topk_w = grad_topk_w;
+  wa.rank_magic = rank_magic(s);
+  wa.T = s.num_tokens;
+  wa.k = s.num_topk;
+  wa.E = s.num_experts;
+  wa.R = s.num_ranks;
+  wa.num_rows = num_recv_rows;
+  const int64_t n = (int64_t)s.num_tokens * s.num_topk;
+  hipLaunchKernelGGL(moe::gather_weight_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, wa);
+  return last_launch_status();
 }
 
 }  // extern "C"

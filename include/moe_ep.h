@@ -208,6 +208,42 @@ moe_status moe_combine_ll(const moe_shape* shape, const void* y, int32_t expert_
                           const int32_t* topk_idx, const float* topk_w, const int32_t* slot_pos,
                           void* out, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Backward (training).  [DeepEP overview: the library serves training; its
+ * backward path needs its own integration.]  Each is the adjoint of the
+ * forward step above, on the rank layout.
+ * ------------------------------------------------------------------------ */
+
+/* Combine backward.
+ *   grad_out     in  bf16[T, H]             gradient of the combine output
+ *   y            in  bf16[num_y_rows, H]    the combine's expert outputs
+ *   topk_idx, topk_w, send_row              as given to moe_combine
+ *   grad_y       out bf16[num_y_rows, H]    row send_row[t, r] = BF16_RNE(fp32 sum over the
+ *                                           slots j of t on rank r, ascending, of
+ *                                           fl32(topk_w[t, j] * grad_out[t])); rows no slot
+ *                                           refers to are not written
+ *   grad_topk_w  out float[T, k]            <grad_out[t], y[row(t, j)]> summed in fp32 in a
+ *                                           fixed order (deterministic); 0 for invalid slots
+ */
+moe_status moe_combine_backward(const moe_shape* shape, const void* grad_out, const void* y, int32_t num_y_rows,
+                                const int32_t* topk_idx, const float* topk_w, const int32_t* send_row,
+                                void* grad_y, float* grad_topk_w, hipStream_t stream);
+
+/* Dispatch backward.
+ *   grad_recv_x       in  bf16[num_recv_rows, H]   gradient w.r.t. the received rows (FP8
+ *                                                  dispatch is passed straight through)
+ *   grad_recv_topk_w  in  float[num_recv_rows, k]  gradient w.r.t. recv_topk_w, or NULL
+ *   topk_idx, send_row                             as given to / returned by moe_dispatch
+ *   grad_x            out bf16[T, H]    BF16_RNE(fp32 sum over ranks r ascending of
+ *                                       grad_recv_x[send_row[t, r]]); +0 for unsent tokens
+ *   grad_topk_w       out float[T, k]   grad_recv_topk_w[row(t, j), j], 0 for invalid slots;
+ *                                       NULL exactly when grad_recv_topk_w is NULL
+ */
+moe_status moe_dispatch_backward(const moe_shape* shape, const void* grad_recv_x, int32_t num_recv_rows,
+                                 const float* grad_recv_topk_w, const int32_t* topk_idx,
+                                 const int32_t* send_row, void* grad_x, float* grad_topk_w,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

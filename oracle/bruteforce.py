@@ -213,3 +213,49 @@ def ll_combine(y_bits: np.ndarray, topk_idx: List[List[int]], topk_w: List[List[
             row_out.append(bf16_round(acc))
         out.append(row_out)
     return out
+
+
+def combine_backward(g_bits, y_bits, topk_idx, topk_w, send_row, E: int, R: int, num_rows: int):
+    """grad_y (bf16 bits, lists) and grad_w (Python floats, exact sums of fp64 products)."""
+    L = E // R
+    H = g_bits.shape[1]
+    grad_y = [[0] * H for _ in range(num_rows)]
+    acc = {}
+    for t, ids in enumerate(topk_idx):
+        for j, e in enumerate(ids):
+            if 0 <= e < E:
+                i = send_row[t][e // L]
+                row = acc.setdefault(i, [0.0] * H)
+                for c in range(H):
+                    row[c] = fl32(row[c] + fl32(fl32(topk_w[t][j]) * bf16_value(int(g_bits[t, c]))))
+    for i, row in acc.items():
+        grad_y[i] = [bf16_round(v) for v in row]
+    grad_w = []
+    for t, ids in enumerate(topk_idx):
+        gw = []
+        for j, e in enumerate(ids):
+            if 0 <= e < E:
+                i = send_row[t][e // L]
+                gw.append(math.fsum(bf16_value(int(g_bits[t, c])) * bf16_value(int(y_bits[i, c])) for c in range(H)))
+            else:
+                gw.append(0.0)
+        grad_w.append(gw)
+    return grad_y, grad_w
+
+
+def dispatch_backward(grad_recv_bits, grad_recv_w, topk_idx, send_row, E: int, R: int):
+    L = E // R
+    H = grad_recv_bits.shape[1]
+    grad_x = []
+    for t, rows in enumerate(send_row):
+        out = []
+        for c in range(H):
+            acc = 0.0
+            for r in range(R):
+                if rows[r] >= 0:
+                    acc = fl32(acc + bf16_value(int(grad_recv_bits[rows[r], c])))
+            out.append(bf16_round(acc))
+        grad_x.append(out)
+    gw = [[fl32(grad_recv_w[send_row[t][e // L]][j]) if 0 <= e < E else 0.0 for j, e in enumerate(ids)]
+          for t, ids in enumerate(topk_idx)]
+    return grad_x, gw

@@ -276,6 +276,63 @@ def ll_combine(y_bits: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, slo
     return f32_to_bf16_bits_rne(acc)
 
 
+# ----------------------------------------------------------------------------------------------
+# Backward (training).  [DeepEP overview: the library serves training as well as inference and its
+# backward path needs its own integration; overlap notes: the kernels target training and prefill.]
+# The pages give no formulas; the backward of each forward step is its adjoint (readings):
+#  11. combine backward, for receive row i = send_row[t, r]:
+#        grad_y[i, c] = BF16_RNE(fp32 sum, j ascending over valid slots of t on rank r, of
+#                       fl32(w_tj * g[t, c]))
+#      and grad_w[t, j] = sum_c g[t, c] * y[row(t, j), c] (a dot product over H; the exact value is
+#      the reference, computed in fp64; invalid slots get 0);
+#  12. dispatch backward: grad_x[t, c] = BF16_RNE(fp32 sum, r ascending over ranks t was sent to, of
+#      grad_recv[send_row[t, r], c]); grad_topk_w[t, j] = grad_recv_topk_w[send_row[t, rank(e_tj)], j]
+#      for valid slots, else 0 (the weight was forwarded unchanged).
+
+def combine_backward(g_bits: np.ndarray, y_bits: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray,
+                     send_row: np.ndarray, num_experts: int, num_ranks: int, num_rows: int
+                     ) -> Tuple[np.ndarray, np.ndarray]:
+    """grad_y bf16 bits [num_rows, H] (reading 11) and grad_w fp64 [T, k] (exact dot products)."""
+    T, k = topk_idx.shape
+    H = g_bits.shape[1]
+    valid, rank = expert_ranks(topk_idx, num_experts, num_ranks)
+    g = bf16_bits_to_f32(g_bits)
+    acc = np.zeros((num_rows, H), dtype=np.float32)
+    for j in range(k):  # ascending slots: each adds its term to the row of its rank
+        ok = valid[:, j]
+        tt = np.nonzero(ok)[0]
+        rows = send_row[tt, rank[tt, j]]
+        prod = (topk_w[tt, j][:, None].astype(np.float32) * g[tt]).astype(np.float32)
+        acc[rows] = (acc[rows] + prod).astype(np.float32)  # rows are distinct within one j
+    grad_y = f32_to_bf16_bits_rne(acc)
+    grad_w = np.zeros((T, k), dtype=np.float64)
+    yf = bf16_bits_to_f32(y_bits).astype(np.float64)
+    for j in range(k):
+        tt = np.nonzero(valid[:, j])[0]
+        rows = send_row[tt, rank[tt, j]]
+        grad_w[tt, j] = (g[tt].astype(np.float64) * yf[rows]).sum(axis=1)
+    return grad_y, grad_w
+
+
+def dispatch_backward(grad_recv_bits: np.ndarray, grad_recv_w: np.ndarray, topk_idx: np.ndarray,
+                      send_row: np.ndarray, num_experts: int, num_ranks: int
+                      ) -> Tuple[np.ndarray, np.ndarray]:
+    """grad_x bf16 bits [T, H] and grad_topk_w fp32 [T, k] (reading 12)."""
+    T, R = send_row.shape
+    H = grad_recv_bits.shape[1]
+    acc = np.zeros((T, H), dtype=np.float32)
+    gr = bf16_bits_to_f32(grad_recv_bits)
+    for r in range(R):  # ascending ranks
+        tt = np.nonzero(send_row[:, r] >= 0)[0]
+        acc[tt] = (acc[tt] + gr[send_row[tt, r]]).astype(np.float32)
+    valid, rank = expert_ranks(topk_idx, num_experts, num_ranks)
+    gw = np.zeros(topk_idx.shape, dtype=np.float32)
+    for j in range(topk_idx.shape[1]):
+        tt = np.nonzero(valid[:, j])[0]
+        gw[tt, j] = grad_recv_w[send_row[tt, rank[tt, j]], j]
+    return f32_to_bf16_bits_rne(acc), gw
+
+
 def run_all(x_bits: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, num_experts: int,
             num_ranks: int, dtype: str) -> Dict[str, np.ndarray]:
     """Layout, slots, metadata and payload for one workload, as a dict of arrays."""

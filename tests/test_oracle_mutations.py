@@ -11,6 +11,7 @@ import pytest
 
 from oracle import moe_oracle as O
 from oracle import numerics as N
+from tests import test_oracle_backward as PB
 from tests import test_oracle_ll as PL
 from tests import test_oracle_pins as P
 
@@ -26,6 +27,9 @@ def _pin_suite():
     P.test_identity_round_trip_k1_is_exact()
     P.test_identity_round_trip_weighted(P.W.CONFIG_BY_NAME["tiny"])
     PL.test_golden_low_latency()
+    PB.test_golden_backward()
+    for case in PB.CASES:
+        PB.test_backward_vs_bruteforce(case)
     for case in PL.LL_CASES[:3]:
         PL.test_ll_vs_bruteforce(case, "bf16")
 
@@ -157,7 +161,36 @@ def _ll_combine_once_per_expert(y, idx, w, slot_pos, E, tokens=None):
     return _orig_ll_combine(y, idx, w, pos, E, tokens)
 
 
+_orig_dbwd = O.dispatch_backward
+
+
+def _dbwd_drop_last_rank(gr, grw, idx, send_row, E, R):
+    sr = send_row.copy()
+    sr[:, -1] = -1
+    gx, _ = _orig_dbwd(gr, grw, idx, sr, E, R)
+    return gx, _orig_dbwd(gr, grw, idx, send_row, E, R)[1]
+
+
+def _dbwd_weight_of_first_slot(gr, grw, idx, send_row, E, R):
+    gx, gw = _orig_dbwd(gr, grw, idx, send_row, E, R)
+    valid, rank = O.expert_ranks(idx, E, R)
+    for j in range(idx.shape[1]):
+        tt = np.nonzero(valid[:, j])[0]
+        gw[tt, j] = grw[send_row[tt, rank[tt, j]], 0]
+    return gx, gw
+
+
+_orig_cbwd = O.combine_backward
+
+
+def _cbwd_unweighted(g, y, idx, w, send_row, E, R, n):
+    return _orig_cbwd(g, y, idx, np.ones_like(w), send_row, E, R, n)
+
+
 MUTANTS = {
+    "dispatch_backward_drops_last_rank": ("dispatch_backward", _dbwd_drop_last_rank),
+    "dispatch_backward_weight_slot": ("dispatch_backward", _dbwd_weight_of_first_slot),
+    "combine_backward_unweighted": ("combine_backward", _cbwd_unweighted),
     "ll_positions_per_slot": ("ll_layout", _ll_layout_per_slot),
     "ll_combine_duplicate_once": ("ll_combine", _ll_combine_once_per_expert),
     "rank_is_e_mod_R": ("expert_ranks", _rank_modulo),
