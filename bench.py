@@ -25,7 +25,10 @@ with N = number of receive rows.  The low-latency (per-expert) path, also
 measured on the decode workload:
   dispatch_ll = T*H*2 + T*k*4 + N'*(H*b + S + 4) + E*4 + T*k*4
   combine_ll  = N'*H*2 + T*k*12 + T*H*2
-with N' = rows written into the per-expert buffers.
+with N' = rows written into the per-expert buffers.  The backward (training)
+ops, measured on the main workload:
+  combine_backward  = T*H*2 + N*H*2 + T*k*8 + T*R*4 + N*H*2 + T*k*4
+  dispatch_backward = N*H*2 + T*R*4 + N*k*4 + T*k*4 + T*H*2 + T*k*4
 """
 from __future__ import annotations
 
@@ -67,6 +70,14 @@ def ll_algorithmic_bytes(cfg, n_rows: int) -> dict:
     return {
         "dispatch_ll": T * H * 2 + T * k * 4 + n_rows * (H * b + S + 4) + E * 4 + T * k * 4,
         "combine_ll": n_rows * H * 2 + T * k * 12 + T * H * 2,
+    }
+
+
+def bwd_algorithmic_bytes(cfg, n_recv: int) -> dict:
+    T, H, k, R = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_ranks
+    return {
+        "combine_backward": T * H * 2 + n_recv * H * 2 + T * k * 8 + T * R * 4 + n_recv * H * 2 + T * k * 4,
+        "dispatch_backward": n_recv * H * 2 + T * R * 4 + n_recv * k * 4 + T * k * 4 + T * H * 2 + T * k * 4,
     }
 
 
@@ -140,13 +151,16 @@ class Workload:
                 yield v
 
     def op(self, name, s):
+        self.op_on(name, s, None)
+
+    def op_on(self, name, s, stream):
         moe, cfg = self.moe, self.cfg
         if name == "layout":
-            moe.run_layout(self.shape, s["idx"], s["lay"])
+            moe.run_layout(self.shape, s["idx"], s["lay"], stream)
         elif name == "dispatch":
-            moe.run_dispatch(self.shape, cfg.dispatch_dtype, s["x"], s["idx"], s["w"], s["lay"], s["disp"])
+            moe.run_dispatch(self.shape, cfg.dispatch_dtype, s["x"], s["idx"], s["w"], s["lay"], s["disp"], stream)
         else:
-            moe.moe_combine(self.shape, s["y"], s["idx"], s["w"], s["disp"]["send_row"], s["out"])
+            moe.moe_combine(self.shape, s["y"], s["idx"], s["w"], s["disp"]["send_row"], s["out"], stream)
 
     def time_steps(self, steps: int, warmup: int):
         torch = self.torch
@@ -275,6 +289,135 @@ class LlWorkload(Workload):
         return {o: op_summary(self.bytes[o], per[o], kern[o]) for o in self.OPS_LL}
 
 
+class BwdWorkload(Workload):
+    """Backward of combine and dispatch on the rank layout of the forward workload."""
+
+    OPS_BWD = ("combine_backward", "dispatch_backward")
+
+    def __init__(self, cfg, torch, moe, W, nsets=None):
+        super().__init__(cfg, torch, moe, W, nsets)
+        import numpy as np
+
+        n, T, H, k = self.n_recv, cfg.num_tokens, cfg.hidden, cfg.num_topk
+        g16 = torch.from_numpy(W.draw_expert_outputs(np.random.default_rng(11), T, H).view(np.int16))
+        grw = torch.from_numpy(np.random.default_rng(12).standard_normal((n, k)).astype(np.float32))
+        for s_ in self.sets:
+            self.op("layout", s_)
+            self.op("dispatch", s_)
+            s_["g"] = g16.cuda().view(torch.bfloat16)
+            s_["grad_y"] = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+            s_["grad_w"] = torch.empty((T, k), dtype=torch.float32, device="cuda")
+            s_["grad_recv_w"] = grw.cuda()
+            s_["grad_x"] = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+            s_["grad_topk_w"] = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        self.bytes = bwd_algorithmic_bytes(cfg, n)
+
+    def op(self, name, s):
+        if name == "combine_backward":
+            self.moe.moe_combine_backward(self.shape, s["g"], s["y"], s["idx"], s["w"], s["disp"]["send_row"],
+                                          s["grad_y"], s["grad_w"])
+        elif name == "dispatch_backward":
+            self.moe.moe_dispatch_backward(self.shape, s["y"], s["idx"], s["disp"]["send_row"], s["grad_x"],
+                                           s["grad_recv_w"], s["grad_topk_w"])
+        else:
+            super().op(name, s)
+
+    def time_bwd(self, steps: int, warmup: int):
+        torch = self.torch
+        n = len(self.sets)
+        for i in range(warmup):
+            for name in self.OPS_BWD:
+                self.op(name, self.sets[i % n])
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            s_, e = self.sets[i % n], ev[i]
+            e[0].record()
+            self.op("combine_backward", s_)
+            e[1].record()
+            self.op("dispatch_backward", s_)
+            e[2].record()
+        torch.cuda.synchronize()
+        per = {name: [e[i].elapsed_time(e[i + 1]) for e in ev] for i, name in enumerate(self.OPS_BWD)}
+        kern = self.time_kernels(ops=self.OPS_BWD)
+        return {o: op_summary(self.bytes[o], per[o], kern[o]) for o in self.OPS_BWD}
+
+
+def cu_sweep(wl: "Workload", torch, moe, budgets=(8, 16, 32, 64, 128, 256), reps: int = 20) -> list:
+    """Dispatch and combine on streams restricted to a number of CUs (the analogue of reserving SMs)."""
+    rows = []
+    n = len(wl.sets)
+    for cus in budgets:
+        h = moe.stream_create_cu_range(0, cus)
+        st = torch.cuda.ExternalStream(h)
+        try:
+            res = {"num_cus": cus}
+            for name in ("dispatch", "combine"):
+                for i in range(3):
+                    wl.op_on(name, wl.sets[i % n], h)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                st.synchronize()
+                e0.record(st)
+                for i in range(reps):
+                    wl.op_on(name, wl.sets[i % n], h)
+                e1.record(st)
+                st.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                res[name] = {"us": round(us, 2), "GB_per_s": round(wl.bytes[name] / (us * 1e-6) / 1e9, 1)}
+            rows.append(res)
+            log(f"cu budget {cus}: {res}")
+        finally:
+            st.synchronize()
+            moe.stream_destroy(h)
+    return rows
+
+
+def overlap(wl: "Workload", torch, moe, comm_cus: int, reps: int = 10) -> dict:
+    """Exchange (dispatch + combine) on `comm_cus` CUs while a bf16 GEMM runs on the other CUs."""
+    total = torch.cuda.get_device_properties(0).multi_processor_count
+    hc = moe.stream_create_cu_range(0, comm_cus)
+    hg = moe.stream_create_cu_range(comm_cus, total - comm_cus)
+    sc, sg = torch.cuda.ExternalStream(hc), torch.cuda.ExternalStream(hg)
+    M = 8192
+    a = torch.randn(M, M, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(M, M, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(M, M, device="cuda", dtype=torch.bfloat16)
+    n = len(wl.sets)
+
+    def comm():
+        for i in range(reps):
+            wl.op_on("dispatch", wl.sets[i % n], hc)
+            wl.op_on("combine", wl.sets[i % n], hc)
+
+    def gemm():
+        with torch.cuda.stream(sg):
+            for _ in range(reps):
+                torch.matmul(a, b, out=c)
+
+    def timed(fns):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for f in fns:
+            f()
+        sc.synchronize()
+        sg.synchronize()
+        return (time.perf_counter() - t0) * 1e3
+
+    try:
+        timed([gemm, comm])  # warm-up
+        t_gemm, t_comm, t_both = timed([gemm]), timed([comm]), timed([gemm, comm])
+    finally:
+        torch.cuda.synchronize()
+        moe.stream_destroy(hc)
+        moe.stream_destroy(hg)
+    res = {"comm_cus": comm_cus, "gemm_cus": total - comm_cus, "reps": reps, "gemm": f"bf16 {M}x{M}x{M}",
+           "ms_gemm_alone": round(t_gemm, 3), "ms_exchange_alone": round(t_comm, 3), "ms_both": round(t_both, 3),
+           "overlap_gain": round((t_gemm + t_comm) / t_both, 3)}
+    log(f"overlap: {res}")
+    return res
+
+
 def op_summary(bytes_: int, times_ms, kernel_us: float) -> dict:
     import numpy as np
 
@@ -350,6 +493,10 @@ def main() -> int:
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the graph-replay per-op timing")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a 1 GiB device copy (counter runs)")
     ap.add_argument("--no-low-latency", action="store_true", help="skip the per-expert path on decode")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward ops on the main workload")
+    ap.add_argument("--cu-sweep", action="store_true", help="dispatch/combine on streams limited to 8..256 CUs")
+    ap.add_argument("--overlap", type=int, default=0, metavar="CUS",
+                    help="exchange on CUS CUs concurrently with a bf16 GEMM on the rest")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -378,8 +525,18 @@ def main() -> int:
         ops = {o: op_summary(wl.bytes[o], per[o], kern[o]) for o in OPS}
         res = {"cfg": cfg, "n_recv": wl.n_recv, "ops": ops, "ms_per_step": wall * 1e3 / args.steps,
                "step_bytes": sum(wl.bytes.values()), "sets": len(wl.sets)}
+        if name == args.workload and args.cu_sweep:
+            res["cu_budget"] = cu_sweep(wl, torch, moe)
+        if name == args.workload and args.overlap:
+            res["overlap"] = overlap(wl, torch, moe, args.overlap)
         del wl
         torch.cuda.empty_cache()
+        if name == args.workload and not args.no_backward:
+            log(f"timing the backward ops on {name}")
+            bw = BwdWorkload(cfg, torch, moe, W)
+            res["backward"] = {"ops": bw.time_bwd(args.steps, args.warmup)}
+            del bw
+            torch.cuda.empty_cache()
         if cfg.name == "decode" and not args.no_low_latency:
             log(f"timing the low-latency path on {name}")
             ll = LlWorkload(cfg, torch, moe, W)
@@ -440,6 +597,9 @@ def main() -> int:
             line["secondary"]["low_latency"] = sec["low_latency"]
     if "low_latency" in main_res:
         line["low_latency"] = main_res["low_latency"]
+    for key in ("backward", "cu_budget", "overlap"):
+        if key in main_res:
+            line[key] = main_res[key]
     print(json.dumps(line), flush=True)
     return 0
 

@@ -53,7 +53,7 @@ class MoeError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m combine_get_dispatch_07_amd.build` "
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python combine_get_dispatch_07_amd/build.py` "
                           "(or __graft_entry__.build()); there is no fallback path")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
@@ -80,6 +80,10 @@ def _load() -> ctypes.CDLL:
     lib.moe_combine_backward.restype = ctypes.c_int
     lib.moe_dispatch_backward.argtypes = [SH, P, I32, P, P, P, P, P, P]
     lib.moe_dispatch_backward.restype = ctypes.c_int
+    lib.moe_stream_create_cu_range.argtypes = [I32, I32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.moe_stream_create_cu_range.restype = ctypes.c_int
+    lib.moe_stream_destroy.argtypes = [P]
+    lib.moe_stream_destroy.restype = ctypes.c_int
     return lib
 
 
@@ -220,3 +224,14 @@ def moe_dispatch_backward(shape: MoeShape, grad_recv_x, topk_idx, send_row, grad
         _ptr(grad_x, "grad_x", torch.bfloat16, T * H), _ptr(grad_topk_w, "grad_topk_w", torch.float32, T * k),
         _stream(stream))
     _check("moe_dispatch_backward", code)
+
+
+def stream_create_cu_range(first_cu: int, num_cus: int) -> int:
+    """A HIP stream restricted to CUs [first_cu, first_cu + num_cus); returns its handle."""
+    h = ctypes.c_void_p()
+    _check("moe_stream_create_cu_range", lib.moe_stream_create_cu_range(int(first_cu), int(num_cus), ctypes.byref(h)))
+    return int(h.value or 0)
+
+
+def stream_destroy(handle: int) -> None:
+    _check("moe_stream_destroy", lib.moe_stream_destroy(ctypes.c_void_p(handle)))

@@ -1,6 +1,6 @@
 """Build libmoe_ep.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m combine_get_dispatch_07_amd.build        # or __graft_entry__.build()
+    python combine_get_dispatch_07_amd/build.py        # or __graft_entry__.build()
 
 Flags that matter for results:
 * ``-ffp-contract=off`` (plus ``#pragma clang fp contract(off)`` in the

@@ -18,7 +18,7 @@
 
 namespace moe {
 
-constexpr int kBwdWaves = 4;  // one block per token; wave w takes slices w, w + 4, ...
+constexpr int kBwdMaxWaves = 16;  // upper bound of waves per block (one block per token)
 constexpr int kMaxTopk = 32;
 
 struct CombineBwdArgs {
@@ -34,9 +34,10 @@ struct CombineBwdArgs {
 };
 
 template <int KB>  // slots handled in registers: 8 or 32 (k <= KB)
-__global__ __launch_bounds__(kBwdWaves * kWave) void combine_backward_kernel(CombineBwdArgs a) {
+__global__ __launch_bounds__(kBwdMaxWaves * kWave) void combine_backward_kernel(CombineBwdArgs a) {
 #pragma clang fp contract(off)
-  __shared__ float partial[kBwdWaves][KB];
+  __shared__ float partial[kBwdMaxWaves][KB];
+  const int nwaves = blockDim.x / kWave;  // wave w takes slices w, w + nwaves, ...
   const int t = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -68,16 +69,57 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void combine_backward_kernel(Com
   for (int jj = 0; jj < KB; ++jj) dot[jj] = 0.0f;
 
   const int slices = (a.H8 + kWave - 1) / kWave;
-  for (int s = wave; s < slices; s += kBwdWaves) {
+  const u32x4* grow = reinterpret_cast<const u32x4*>(a.g + (size_t)t * a.H);
+  // k <= 8: software pipeline over this wave's slices -- the next slice's g and
+  // y loads are issued before the current slice's grad_y rows are stored.
+  // k > 8: slots in batches of 8 per slice, without prefetch.
+  constexpr bool kPrefetch = KB <= 8;
+  u32x4 gv, yv[kPrefetch ? KB : 1];
+  auto load_slice = [&](int s_) {
+    const int cc = min(s_ * kWave + lane, a.H8 - 1);
+    gv = grow[cc];
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj)
+        yv[jj] = reinterpret_cast<const u32x4*>(a.y + (size_t)max(srow[jj], 0) * a.H)[cc];
+    }
+  };
+  int s = wave;
+  if (s < slices) load_slice(s);
+  for (; s < slices; s += nwaves) {
     const int c = s * kWave + lane;
     const int cc = min(c, a.H8 - 1);
-    const u32x4 gv = reinterpret_cast<const u32x4*>(a.g + (size_t)t * a.H)[cc];
     float gf[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       gf[2 * i] = bf16_lo(gv[i]);
       gf[2 * i + 1] = bf16_hi(gv[i]);
     }
+    // dot products of g with every slot's y row
+#pragma unroll
+    for (int b = 0; b < KB; b += 8) {
+      u32x4 yb[8];
+      if constexpr (!kPrefetch) {
+        if (b >= a.k) break;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          yb[jj] = reinterpret_cast<const u32x4*>(a.y + (size_t)max(srow[b + jj], 0) * a.H)[cc];
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const u32x4& v = kPrefetch ? yv[jj] : yb[jj];
+        if (srow[b + jj] >= 0 && c < a.H8) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = gf[2 * i] * bf16_lo(v[i]);
+            const float p1 = gf[2 * i + 1] * bf16_hi(v[i]);
+            dot[b + jj] = dot[b + jj] + p0;
+            dot[b + jj] = dot[b + jj] + p1;
+          }
+        }
+      }
+    }
+    if (s + nwaves < slices) load_slice(s + nwaves);  // in flight during the stores below
     // grad_y rows: one per destination rank, its slots added in ascending order
     for (uint64_t todo = ranks; todo; todo &= todo - 1) {
       const int r = __builtin_ctzll(todo);
@@ -98,22 +140,6 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void combine_backward_kernel(Com
       }
       if (c < a.H8) store_out(reinterpret_cast<u32x4*>(a.grad_y + (size_t)dst_row * a.H), c, acc);
     }
-    // dot products of g with every slot's y row
-    if (c < a.H8) {
-#pragma unroll
-      for (int jj = 0; jj < KB; ++jj) {
-        if (srow[jj] >= 0) {
-          const u32x4 yv = reinterpret_cast<const u32x4*>(a.y + (size_t)srow[jj] * a.H)[c];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = gf[2 * i] * bf16_lo(yv[i]);
-            const float p1 = gf[2 * i + 1] * bf16_hi(yv[i]);
-            dot[jj] = dot[jj] + p0;
-            dot[jj] = dot[jj] + p1;
-          }
-        }
-      }
-    }
   }
 
   // fixed-order reductions: across lanes (xor tree), then across the block's waves
@@ -127,8 +153,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void combine_backward_kernel(Com
   __syncthreads();
   if (threadIdx.x < a.k) {  // wave 0, lane j: its own `valid` is slot j's
     float sum = 0.0f;
-#pragma unroll
-    for (int q = 0; q < kBwdWaves; ++q) sum = sum + partial[q][threadIdx.x];
+    for (int q = 0; q < nwaves; ++q) sum = sum + partial[q][threadIdx.x];
     a.grad_w[(size_t)t * a.k + threadIdx.x] = valid ? sum : 0.0f;
   }
 }

@@ -3,6 +3,7 @@
 // Everything is checked before the first HIP call, so a rejected call touches
 // neither the GPU nor any memory.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -26,6 +27,7 @@ constexpr int kMaxRanks = 64;
 constexpr int kMaxExperts = 4096;
 constexpr size_t kPlanAlign = 256;
 constexpr int kMaxDevices = 64;
+constexpr int kMaxCuMaskWords = 32;  // up to 1024 compute units
 // Wide FP8 dispatch slices only when they still give this many waves.
 constexpr long kMinFp8Waves = 4096;
 
@@ -109,6 +111,12 @@ void launch_dispatch(int U, dim3 grid, hipStream_t stream, const moe::DispatchAr
   }
 }
 
+// Waves per token in the combine backward (each takes every MOE_BWD_WAVES-th slice).
+#ifndef MOE_BWD_WAVES
+#define MOE_BWD_WAVES 4
+#endif
+static_assert(MOE_BWD_WAVES >= 1 && MOE_BWD_WAVES <= moe::kBwdMaxWaves, "waves per block");
+
 // Resident combine waves per CU in the persistent launch (2 per SIMD, each
 // with two items' payload in flight).
 #ifndef MOE_COMBINE_WAVES_PER_CU
@@ -126,6 +134,29 @@ int device_cu_count() {
     return 256;
   cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+// Compute units a launch on `stream` can use: the popcount of the stream's CU
+// mask (all of the device's CUs for an unrestricted stream).
+int stream_cu_count(hipStream_t stream) {
+  uint32_t mask[kMaxCuMaskWords] = {0};
+  if (stream == nullptr || hipExtStreamGetCUMask(stream, kMaxCuMaskWords, mask) != hipSuccess) {
+    (void)hipGetLastError();
+    return device_cu_count();
+  }
+  int n = 0;
+  for (uint32_t w : mask) n += __builtin_popcount(w);
+  return n > 0 ? std::min(n, device_cu_count()) : device_cu_count();
+}
+
+int device_xcc_count() {
+  int dev = 0, xcc = 1;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcc <= 0) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  return xcc;
 }
 
 __global__ __launch_bounds__(256) void zero_fill_kernel(moe::u32x4* p, size_t n16) {
@@ -147,7 +178,7 @@ moe_status launch_combine(moe::CombineArgs& a, void* out, hipStream_t stream) {
   if ((int64_t)a.T * a.slices > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   a.items = a.T * a.slices;
   const int waves_per_block = moe::kCombineBlock / moe::kWave;
-  const long resident = (long)device_cu_count() * MOE_COMBINE_WAVES_PER_CU / waves_per_block;
+  const long resident = (long)stream_cu_count(stream) * MOE_COMBINE_WAVES_PER_CU / waves_per_block;
   const dim3 grid((unsigned)std::min<long>((a.items + waves_per_block - 1) / waves_per_block, resident));
   const dim3 block(moe::kCombineBlock);
   a.terms = kMode == moe::kRankRows ? a.R : a.k;
@@ -512,7 +543,8 @@ moe_status moe_combine_backward(const moe_shape* shape, const void* grad_out, co
   a.E = s.num_experts;
   a.R = s.num_ranks;
   a.num_y_rows = num_y_rows;
-  const dim3 grid(s.num_tokens), block(moe::kBwdWaves * moe::kWave);
+  const int slices = (a.H8 + moe::kWave - 1) / moe::kWave;
+  const dim3 grid(s.num_tokens), block(std::min(slices, MOE_BWD_WAVES) * moe::kWave);
   if (s.num_topk <= 8)
     hipLaunchKernelGGL(moe::combine_backward_kernel<8>, grid, block, 0, stream, a);
   else
@@ -566,6 +598,30 @@ moe_status moe_dispatch_backward(const moe_shape* shape, const void* grad_recv_x
   const int64_t n = (int64_t)s.num_tokens * s.num_topk;
   hipLaunchKernelGGL(moe::gather_weight_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, wa);
   return last_launch_status();
+}
+
+moe_status moe_stream_create_cu_range(int32_t first_cu, int32_t num_cus, hipStream_t* stream) {
+  if (stream == nullptr) return MOE_ERR_INVALID_ARG;
+  *stream = nullptr;
+  const int cus = device_cu_count(), xcc = device_xcc_count();
+  if (first_cu == 0 && (num_cus <= 0 || num_cus >= cus))
+    return hipStreamCreateWithFlags(stream, hipStreamNonBlocking) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  if (first_cu < 0 || num_cus <= 0 || first_cu % xcc != 0 || num_cus % xcc != 0 || first_cu + num_cus > cus ||
+      (cus + 31) / 32 > kMaxCuMaskWords)
+    return MOE_ERR_INVALID_ARG;
+  uint32_t mask[kMaxCuMaskWords] = {0};
+  for (int i = first_cu; i < first_cu + num_cus; ++i) mask[i / 32] |= 1u << (i % 32);
+  if (hipExtStreamCreateWithCUMask(stream, (uint32_t)((cus + 31) / 32), mask) != hipSuccess) {
+    (void)hipGetLastError();  // do not leave the failure for the next unrelated call
+    *stream = nullptr;
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_stream_destroy(hipStream_t stream) {
+  if (stream == nullptr) return MOE_ERR_INVALID_ARG;
+  return hipStreamDestroy(stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // extern "C"

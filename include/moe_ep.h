@@ -244,6 +244,30 @@ moe_status moe_dispatch_backward(const moe_shape* shape, const void* grad_recv_x
                                  const int32_t* send_row, void* grad_x, float* grad_topk_w,
                                  hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Compute-unit budget.  [overlap notes, 节点内通信: DeepEP gives its exchange
+ * kernels a fixed share of the SMs (20 of 132) so that expert computation
+ * overlaps on the rest; DeepEP overview: Buffer.set_num_sms trades exchange
+ * latency against compute.]  The MI355X equivalent is a stream whose kernels
+ * may only run on a chosen set of CUs.  Launches of this library on such a
+ * stream size their persistent grids to that stream's CUs.
+ *
+ * CU-mask bit i of a stream belongs to XCD (i mod number of XCDs) on MI355X,
+ * and every XCD must keep at least one CU; so the range [first_cu,
+ * first_cu + num_cus) must consist of multiples of the XCD count (8), which
+ * gives every XCD the same number of CUs.
+ * ------------------------------------------------------------------------ */
+
+/* Creates (non-blocking, default priority) a stream restricted to CUs
+ * [first_cu, first_cu + num_cus) of the current device.  first_cu == 0 with
+ * num_cus <= 0 or >= the CU count gives an unrestricted stream.  The caller
+ * destroys it with moe_stream_destroy.  MOE_ERR_INVALID_ARG for a range that
+ * is not a multiple of the XCD count or exceeds the device. */
+moe_status moe_stream_create_cu_range(int32_t first_cu, int32_t num_cus, hipStream_t* stream);
+
+/* Destroys a stream made by moe_stream_create_cu_range. */
+moe_status moe_stream_destroy(hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
