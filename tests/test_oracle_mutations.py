@@ -11,9 +11,11 @@ import pytest
 
 from oracle import moe_oracle as O
 from oracle import numerics as N
+from oracle import router as RT
 from tests import test_oracle_backward as PB
 from tests import test_oracle_ll as PL
 from tests import test_oracle_pins as P
+from tests import test_oracle_router as PR
 
 
 def _pin_suite():
@@ -185,6 +187,89 @@ _orig_cbwd = O.combine_backward
 
 def _cbwd_unweighted(g, y, idx, w, send_row, E, R, n):
     return _orig_cbwd(g, y, idx, np.ones_like(w), send_row, E, R, n)
+
+
+def _router_pin_suite():
+    PR.test_golden_router()
+    for case in PR.SMALL:
+        PR.test_router_vs_bruteforce(case)
+        PR.test_router_properties(case)
+
+
+_orig_route = RT.route
+
+
+def _route_ties_to_higher_id(logits, k, gate="softmax", num_groups=1, topk_groups=1):
+    # selection on the experts in reverse id order, mapped back: equal logits prefer the higher id
+    x = np.ascontiguousarray(logits, dtype=np.float32)
+    E = x.shape[1]
+    if num_groups > 1:
+        return _orig_route(x, k, gate, num_groups, topk_groups)
+    idx, w = _orig_route(x[:, ::-1], k, gate, 1, 1)
+    return (E - 1 - idx).astype(np.int32), w
+
+
+def _group_mask_sum_top2(logits, num_groups, topk_groups):
+    T, E = logits.shape
+    S = E // num_groups
+    g = np.sort(logits.reshape(T, num_groups, S).astype(np.float64), axis=2)
+    score = g[:, :, -1] + (g[:, :, -2] if S > 1 else 0.0)
+    order = np.lexsort((np.broadcast_to(np.arange(num_groups), score.shape), -score), axis=1)
+    keep = np.zeros((T, num_groups), dtype=bool)
+    np.put_along_axis(keep, order[:, :topk_groups], True, axis=1)
+    return np.repeat(keep, S, axis=1)
+
+
+def _group_mask_ties_to_higher_group(logits, num_groups, topk_groups):
+    T, E = logits.shape
+    S = E // num_groups
+    score = logits.reshape(T, num_groups, S).max(axis=2).astype(np.float64)
+    order = np.lexsort((np.broadcast_to(-np.arange(num_groups), score.shape), -score), axis=1)
+    keep = np.zeros((T, num_groups), dtype=bool)
+    np.put_along_axis(keep, order[:, :topk_groups], True, axis=1)
+    return np.repeat(keep, S, axis=1)
+
+
+def _route_softmax_over_all(logits, k, gate="softmax", num_groups=1, topk_groups=1):
+    idx, w = _orig_route(logits, k, gate, num_groups, topk_groups)
+    if gate != "softmax":
+        return idx, w
+    x = np.asarray(logits, dtype=np.float64)
+    p = np.exp(x - x.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    return idx, np.take_along_axis(p, idx.astype(np.int64), axis=1).astype(np.float32)
+
+
+def _route_sigmoid_unnormalised(logits, k, gate="softmax", num_groups=1, topk_groups=1):
+    idx, w = _orig_route(logits, k, gate, num_groups, topk_groups)
+    if gate != "sigmoid":
+        return idx, w
+    sel = np.take_along_axis(np.asarray(logits, dtype=np.float64), idx.astype(np.int64), axis=1)
+    return idx, (1.0 / (1.0 + np.exp(-sel))).astype(np.float32)
+
+
+def _route_signed_zero_order(logits, k, gate="softmax", num_groups=1, topk_groups=1):
+    x = np.array(logits, dtype=np.float32)
+    x[(x == 0) & np.signbit(x)] = np.float32(-1e-30)  # -0.0 ranked below +0.0
+    return _orig_route(x, k, gate, num_groups, topk_groups)
+
+
+ROUTER_MUTANTS = {
+    "router_ties_to_higher_id": ("route", _route_ties_to_higher_id),
+    "router_group_score_sum_top2": ("group_mask", _group_mask_sum_top2),
+    "router_group_ties_to_higher_group": ("group_mask", _group_mask_ties_to_higher_group),
+    "router_softmax_over_all_experts": ("route", _route_softmax_over_all),
+    "router_sigmoid_not_normalised": ("route", _route_sigmoid_unnormalised),
+    "router_negative_zero_below_positive_zero": ("route", _route_signed_zero_order),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROUTER_MUTANTS))
+def test_router_pins_catch_mutant(name, monkeypatch):
+    attr, fn = ROUTER_MUTANTS[name]
+    monkeypatch.setattr(RT, attr, fn)
+    with pytest.raises(AssertionError):
+        _router_pin_suite()
 
 
 MUTANTS = {

@@ -22,6 +22,11 @@ configurations this library is measured on; their routing recipes are:
   1-based permutation of the experts.  Gumbel-top-k is Plackett-Luce sampling
   without replacement, so the first pick is exactly Zipf(s).
 
+The GPU gate (top-k fused with the layout) is a method step of its own: it is
+checked against ``oracle/router.py`` on the logits drawn here
+(:func:`config_logits`), never against the routing code of this module, which
+only synthesises ids and weights for the layout, dispatch and combine steps.
+
 Bit patterns of bf16 are carried as ``numpy.uint16``; fp32 -> bf16 uses torch's
 round-to-nearest-even conversion (a library routine).
 """
@@ -42,6 +47,8 @@ __all__ = [
     "bf16_bits_from_f32",
     "draw_hidden",
     "draw_expert_outputs",
+    "draw_logits",
+    "config_logits",
     "route",
     "make_inputs",
     "random_case",
@@ -138,11 +145,11 @@ def _sigmoid_normalised(sel_logits: np.ndarray) -> np.ndarray:
     return (s / s.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
-def route(cfg: Config, gen_router: np.random.Generator, gen_extra: np.random.Generator,
-          num_tokens: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """Top-k expert ids (int32 [T, k]) and gate weights (fp32 [T, k]) for ``cfg``."""
+def draw_logits(cfg: Config, gen_router: np.random.Generator, gen_extra: np.random.Generator,
+                num_tokens: Optional[int] = None) -> np.ndarray:
+    """Router logits fp32 [T, E] for ``cfg`` (N(0,1), or the Zipf-skewed Gumbel form)."""
     T = cfg.num_tokens if num_tokens is None else num_tokens
-    E, k = cfg.num_experts, cfg.num_topk
+    E = cfg.num_experts
     if cfg.routing == "zipf":
         perm = gen_extra.permutation(E)
         pos = np.empty(E, dtype=np.float64)
@@ -150,9 +157,22 @@ def route(cfg: Config, gen_router: np.random.Generator, gen_extra: np.random.Gen
         u = gen_router.random((T, E))
         u = np.clip(u, np.finfo(np.float64).tiny, 1.0 - 2.0 ** -53)
         gumbel = -np.log(-np.log(u))
-        logits = (-cfg.zipf_s * np.log(pos)[None, :] + gumbel).astype(np.float32)
-    else:
-        logits = gen_router.standard_normal((T, E), dtype=np.float32)
+        return (-cfg.zipf_s * np.log(pos)[None, :] + gumbel).astype(np.float32)
+    return gen_router.standard_normal((T, E), dtype=np.float32)
+
+
+def config_logits(cfg: Config, num_tokens: Optional[int] = None) -> np.ndarray:
+    """The logits :func:`make_inputs` routes for ``cfg`` (drawn for ``num_tokens`` tokens if given)."""
+    _g_x, g_router, _g_y, g_extra = seed_streams(cfg.index)
+    return draw_logits(cfg, g_router, g_extra, num_tokens)
+
+
+def route(cfg: Config, gen_router: np.random.Generator, gen_extra: np.random.Generator,
+          num_tokens: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k expert ids (int32 [T, k]) and gate weights (fp32 [T, k]) for ``cfg``."""
+    T = cfg.num_tokens if num_tokens is None else num_tokens
+    E, k = cfg.num_experts, cfg.num_topk
+    logits = draw_logits(cfg, gen_router, gen_extra, T)
 
     if cfg.routing == "group_limited":
         G = cfg.num_groups
