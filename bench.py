@@ -344,6 +344,74 @@ class BwdWorkload(Workload):
         return {o: op_summary(self.bytes[o], per[o], kern[o]) for o in self.OPS_BWD}
 
 
+def graph_us(torch, fn, reps: int = 20, repeats: int = 5) -> float:
+    """Median µs per call of `fn(r)` from a HIP graph of `reps` back-to-back calls."""
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for r in range(reps):
+            fn(r)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(reps):
+                fn(r)
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / reps)
+    del g
+    return sorted(times)[len(times) // 2]
+
+
+def router_timing(cfg, torch, moe, W, nsets: int = 8) -> dict:
+    """Top-k gating fused with the layout against the layout alone on the same ids, and against a
+    plain torch gate (topk + softmax/sigmoid, no group limit) for context."""
+    grouped = cfg.routing == "group_limited"
+    gate = "sigmoid" if cfg.routing == "sigmoid" else "softmax"
+    G, KG = (cfg.num_groups, cfg.topk_groups) if grouped else (1, 1)
+    shape = moe.MoeShape(cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks)
+    logits = torch.from_numpy(W.config_logits(cfg)).cuda()
+    sets = []
+    for _ in range(nsets):
+        lay = moe.alloc_route(shape)
+        sets.append({"logits": logits.clone(), "lay": lay})
+    for s in sets:
+        moe.run_route(shape, s["logits"], s["lay"], gate, G, KG)
+    torch.cuda.synchronize()
+
+    def fused(r):
+        s = sets[r % nsets]
+        moe.run_route(shape, s["logits"], s["lay"], gate, G, KG)
+
+    def layout_only(r):
+        s = sets[r % nsets]
+        moe.run_layout(shape, s["lay"]["topk_idx"], s["lay"])
+
+    def torch_gate(r):
+        x = sets[r % nsets]["logits"]
+        v, _ = torch.topk(x, cfg.num_topk, dim=1)
+        w = torch.softmax(v, dim=1) if gate == "softmax" else torch.sigmoid(v)
+        if gate == "sigmoid":
+            w = w / w.sum(dim=1, keepdim=True)
+
+    T, E, k, R = cfg.num_tokens, cfg.num_experts, cfg.num_topk, cfg.num_ranks
+    nbytes = T * E * 4 + T * k * 8 + T * R + T * 8
+    out = {"gate": gate, "num_groups": G, "topk_groups": KG,
+           "route_layout_us": round(graph_us(torch, fused), 2),
+           "layout_only_us": round(graph_us(torch, layout_only), 2),
+           "torch_topk_gate_us": round(graph_us(torch, torch_gate), 2),
+           "algorithmic_bytes": nbytes}
+    out["route_layout_GB_per_s"] = round(nbytes / (out["route_layout_us"] * 1e-6) / 1e9, 1)
+    return out
+
+
 def cu_sweep(wl: "Workload", torch, moe, budgets=(8, 16, 32, 64, 128, 256), reps: int = 20) -> list:
     """Dispatch and combine on streams restricted to a number of CUs (the analogue of reserving SMs)."""
     rows = []
@@ -494,6 +562,7 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true", help="also run a 1 GiB device copy (counter runs)")
     ap.add_argument("--no-low-latency", action="store_true", help="skip the per-expert path on decode")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward ops on the main workload")
+    ap.add_argument("--no-router", action="store_true", help="skip the fused router + layout timing")
     ap.add_argument("--cu-sweep", action="store_true", help="dispatch/combine on streams limited to 8..256 CUs")
     ap.add_argument("--overlap", type=int, default=0, metavar="CUS",
                     help="exchange on CUS CUs concurrently with a bf16 GEMM on the rest")
@@ -536,6 +605,10 @@ def main() -> int:
             bw = BwdWorkload(cfg, torch, moe, W)
             res["backward"] = {"ops": bw.time_bwd(args.steps, args.warmup)}
             del bw
+            torch.cuda.empty_cache()
+        if not args.no_router:
+            log(f"timing the fused router + layout on {name}")
+            res["router"] = router_timing(cfg, torch, moe, W)
             torch.cuda.empty_cache()
         if cfg.name == "decode" and not args.no_low_latency:
             log(f"timing the low-latency path on {name}")
@@ -593,11 +666,12 @@ def main() -> int:
                                          f"top-{c2.num_topk} R={c2.num_ranks} {c2.dispatch_dtype} dispatch",
                              "n_recv": sec["n_recv"], "ms_per_step": round(sec["ms_per_step"], 4),
                              "ops": sec["ops"]}
-        if "low_latency" in sec:
-            line["secondary"]["low_latency"] = sec["low_latency"]
+        for key in ("low_latency", "router"):
+            if key in sec:
+                line["secondary"][key] = sec[key]
     if "low_latency" in main_res:
         line["low_latency"] = main_res["low_latency"]
-    for key in ("backward", "cu_budget", "overlap"):
+    for key in ("backward", "cu_budget", "overlap", "router"):
         if key in main_res:
             line[key] = main_res[key]
     print(json.dumps(line), flush=True)

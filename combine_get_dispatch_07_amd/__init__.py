@@ -15,7 +15,7 @@ import torch
 
 from ._lib import (LIB_PATH, MoeError, MoeShape, ll_workspace_bytes, max_recv_rows, moe_combine,  # noqa: F401
                    moe_combine_backward, moe_combine_ll, moe_dispatch, moe_dispatch_backward, moe_dispatch_ll,
-                   moe_get_dispatch_layout, status_string, stream_create_cu_range, stream_destroy,
+                   moe_get_dispatch_layout, moe_route_layout, status_string, stream_create_cu_range, stream_destroy,
                    workspace_bytes)
 
 
@@ -27,6 +27,20 @@ def alloc_layout(shape: MoeShape, device="cuda") -> Dict[str, torch.Tensor]:
         "is_token_in_rank": torch.empty((shape.num_tokens, shape.num_ranks), dtype=torch.uint8, device=device),
         "workspace": torch.empty(workspace_bytes(shape), dtype=torch.uint8, device=device),
     }
+
+
+def alloc_route(shape: MoeShape, device="cuda") -> Dict[str, torch.Tensor]:
+    """Outputs of moe_route_layout: the routing (ids, weights) plus everything alloc_layout holds."""
+    lay = alloc_layout(shape, device)
+    lay["topk_idx"] = torch.empty((shape.num_tokens, shape.num_topk), dtype=torch.int32, device=device)
+    lay["topk_w"] = torch.empty((shape.num_tokens, shape.num_topk), dtype=torch.float32, device=device)
+    return lay
+
+
+def run_route(shape: MoeShape, logits: torch.Tensor, lay: Dict[str, torch.Tensor], gate: str = "softmax",
+              num_groups: int = 1, topk_groups: int = 1, stream=None) -> None:
+    moe_route_layout(shape, logits, lay["topk_idx"], lay["topk_w"], lay["tokens_per_rank"], lay["tokens_per_expert"],
+                     lay["is_token_in_rank"], lay["workspace"], gate, num_groups, topk_groups, stream)
 
 
 def alloc_dispatch(shape: MoeShape, dtype: str, device="cuda", capacity: Optional[int] = None) -> Dict[str, torch.Tensor]:

@@ -27,10 +27,18 @@ MOE_BF16 = 0
 MOE_FP8_E4M3 = 1
 DTYPES = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
+MOE_GATE_SOFTMAX = 0
+MOE_GATE_SIGMOID = 1
+GATES = {"softmax": MOE_GATE_SOFTMAX, "sigmoid": MOE_GATE_SIGMOID}
+
 
 class MoeShapeC(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("num_topk", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("num_ranks", ctypes.c_int32)]
+
+
+class MoeRouterC(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_int32), ("num_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -66,6 +74,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_max_recv_rows.restype = I32
     lib.moe_get_dispatch_layout.argtypes = [SH, P, P, P, P, P, SZ, P]
     lib.moe_get_dispatch_layout.restype = ctypes.c_int
+    lib.moe_route_layout.argtypes = [SH, ctypes.POINTER(MoeRouterC), P, P, P, P, P, P, P, SZ, P]
+    lib.moe_route_layout.restype = ctypes.c_int
     lib.moe_dispatch.argtypes = [SH, ctypes.c_int, P, P, P, P, SZ, I32, P, P, P, P, P, P, P, P, P]
     lib.moe_dispatch.restype = ctypes.c_int
     lib.moe_combine.argtypes = [SH, P, I32, P, P, P, P, P]
@@ -143,6 +153,21 @@ def moe_get_dispatch_layout(shape: MoeShape, topk_idx, tokens_per_rank, tokens_p
         _ptr(is_token_in_rank, "is_token_in_rank", torch.uint8, T * R),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
     _check("moe_get_dispatch_layout", code)
+
+
+def moe_route_layout(shape: MoeShape, logits, topk_idx, topk_w, tokens_per_rank, tokens_per_expert,
+                     is_token_in_rank, workspace, gate: str = "softmax", num_groups: int = 1, topk_groups: int = 1,
+                     stream=None) -> None:
+    T, k, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
+    router = MoeRouterC(GATES[gate], int(num_groups), int(topk_groups))
+    code = lib.moe_route_layout(
+        ctypes.byref(shape.c()), ctypes.byref(router), _ptr(logits, "logits", torch.float32, T * E),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
+        _ptr(tokens_per_rank, "tokens_per_rank", torch.int32, R),
+        _ptr(tokens_per_expert, "tokens_per_expert", torch.int32, E),
+        _ptr(is_token_in_rank, "is_token_in_rank", torch.uint8, T * R),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check("moe_route_layout", code)
 
 
 def moe_dispatch(shape: MoeShape, dtype: str, x, topk_idx, topk_w, workspace, recv_x, recv_scales, recv_src_idx,

@@ -156,12 +156,22 @@ __global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a
 // Multi-block path, pass 2 (one block): expert totals, per-rank chunk prefix, rank offsets.
 __global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutArgs a) {
   __shared__ int rank_total[kWave];
+  __shared__ int part_sum[1024];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int nwaves = blockDim.x >> 6;
-  for (int e = tid; e < a.E; e += blockDim.x) {
+  // Expert totals: with E < blockDim, P = blockDim / E threads per expert each
+  // sum every P-th block row (independent loads, many in flight), then one
+  // thread adds the P partials.  Integer sums: the order does not matter.
+  const int P = a.E >= (int)blockDim.x ? 1 : (int)blockDim.x / a.E;
+  for (int i = tid; i < P * a.E; i += blockDim.x) {
+    const int e = i % a.E, part = i / a.E;
     int s = 0;
-    for (int b = 0; b < a.NB; ++b) s += a.block_expert[(size_t)b * a.E + e];
-    a.tokens_per_expert[e] = s;
+#pragma unroll 8
+    for (int b = part; b < a.NB; b += P) s += a.block_expert[(size_t)b * a.E + e];
+    if (P == 1)
+      a.tokens_per_expert[e] = s;
+    else
+      part_sum[i] = s;
   }
   for (int r = wave; r < a.R; r += nwaves) {
     int* row = a.chunk_base + (size_t)r * a.NC;
@@ -176,6 +186,13 @@ __global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutArgs a) {
     if (lane == 0) rank_total[r] = carry;
   }
   __syncthreads();
+  if (P > 1) {
+    for (int e = tid; e < a.E; e += blockDim.x) {
+      int s = 0;
+      for (int q = 0; q < P; ++q) s += part_sum[q * a.E + e];
+      a.tokens_per_expert[e] = s;
+    }
+  }
   if (wave == 0) publish_rank_offsets(a, rank_total, lane);
 }
 

@@ -19,6 +19,7 @@
 #include "dispatch_kernels.h"
 #include "layout_kernels.h"
 #include "ll_kernels.h"
+#include "router_kernels.h"
 
 namespace {
 
@@ -60,8 +61,8 @@ PlanLayout plan_layout(const moe_shape& s) {
   off = align_up(off + T * sizeof(uint64_t), kPlanAlign);
   p.chunk_base = off;
   off = align_up(off + R * (size_t)p.NC * sizeof(int32_t), kPlanAlign);
-  p.block_expert = off;
-  off = align_up(off + (size_t)p.NB * E * sizeof(int32_t), kPlanAlign);
+  p.block_expert = off;  // one histogram row per 64-token chunk (router path); NB <= NC
+  off = align_up(off + (size_t)std::max(p.NC, p.NB) * E * sizeof(int32_t), kPlanAlign);
   p.rank_offsets = off;
   off = align_up(off + (R + 1) * sizeof(int32_t), kPlanAlign);
   p.total = off;
@@ -218,6 +219,28 @@ void launch_ll_dispatch(int U, dim3 grid, hipStream_t stream, const moe::LlDispa
   }
 }
 
+
+template <int VMAX, int KL>
+void launch_router(bool fused, int T, size_t lds, hipStream_t stream, const moe::RouterArgs& a) {
+  if (fused) {
+    const int waves = std::max(1, (T + moe::kRouterTokensPerWave - 1) / moe::kRouterTokensPerWave);
+    hipLaunchKernelGGL((moe::router_layout_fused_kernel<VMAX, KL>), dim3(1), dim3(waves * moe::kWave), lds,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((moe::router_count_kernel<VMAX, KL>), dim3(a.lay.NC), dim3(moe::kRouterBlock), lds,
+                       stream, a);
+    hipLaunchKernelGGL(moe::layout_finalize_kernel, dim3(1), dim3(1024), 0, stream, a.lay);
+  }
+}
+
+template <int VMAX>
+void launch_router_v(int k, bool fused, int T, size_t lds, hipStream_t stream, const moe::RouterArgs& a) {
+  if (k <= 8)
+    launch_router<VMAX, 8>(fused, T, lds, stream, a);
+  else
+    launch_router<VMAX, 16>(fused, T, lds, stream, a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,6 +312,70 @@ moe_status moe_get_dispatch_layout(const moe_shape* shape, const int32_t* topk_i
                        stream, a);
     hipLaunchKernelGGL(moe::layout_finalize_kernel, dim3(1), dim3(1024), 0, stream, a);
   }
+  return last_launch_status();
+}
+
+moe_status moe_route_layout(const moe_shape* shape, const moe_router* router, const float* logits,
+                            int32_t* topk_idx, float* topk_w, int32_t* tokens_per_rank,
+                            int32_t* tokens_per_expert, uint8_t* is_token_in_rank, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (router == nullptr) return MOE_ERR_INVALID_ARG;
+  const moe_shape s = *shape;
+  const int64_t T = s.num_tokens;
+  const int E = s.num_experts, k = s.num_topk, G = router->num_groups, KG = router->topk_groups;
+  if (router->gate != MOE_GATE_SOFTMAX && router->gate != MOE_GATE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (G < 1 || KG < 1 || KG > G) return MOE_ERR_INVALID_ARG;
+  if (E % 8 != 0 || E > moe::kRouterMaxExperts || k > 16) return MOE_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return MOE_ERR_UNSUPPORTED;
+  if (E % G != 0 || k > KG * (E / G)) return MOE_ERR_INVALID_ARG;
+  if (!present(logits, T) || !present(topk_idx, T) || !present(topk_w, T) || !present(is_token_in_rank, T) ||
+      !tokens_per_rank || !tokens_per_expert || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(tokens_per_rank, 4) ||
+      !aligned(tokens_per_expert, 4) || !aligned(workspace, kPlanAlign))
+    return MOE_ERR_INVALID_ARG;
+  const PlanLayout p = plan_layout(s);
+  if (workspace_bytes < p.total) return MOE_ERR_INVALID_ARG;
+
+  char* ws = static_cast<char*>(workspace);
+  moe::RouterArgs a{};
+  a.logits = logits;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.lay.topk_idx = topk_idx;
+  a.lay.tokens_per_rank = tokens_per_rank;
+  a.lay.tokens_per_expert = tokens_per_expert;
+  a.lay.mask = is_token_in_rank;
+  a.lay.token_ranks = reinterpret_cast<uint64_t*>(ws + p.token_ranks);
+  a.lay.chunk_base = reinterpret_cast<int32_t*>(ws + p.chunk_base);
+  a.lay.block_expert = reinterpret_cast<int32_t*>(ws + p.block_expert);
+  a.lay.ws_rank_offsets = reinterpret_cast<int32_t*>(ws + p.rank_offsets);
+  a.lay.rank_magic = rank_magic(s);
+  a.lay.T = s.num_tokens;
+  a.lay.k = k;
+  a.lay.E = E;
+  a.lay.R = s.num_ranks;
+  a.lay.NC = p.NC;
+  a.lay.NB = p.NC;  // one expert histogram row per routed 64-token chunk
+  a.lay.mask_words = (s.num_ranks % 4 == 0 && aligned(is_token_in_rank, 4)) ? 1 : 0;
+  a.V = E / 8;
+  a.G = G;
+  a.KG = KG;
+  a.sigmoid = router->gate == MOE_GATE_SIGMOID ? 1 : 0;
+  a.vec4 = (a.V % 4 == 0 && aligned(logits, 16)) ? 1 : 0;
+
+  const bool fused = T <= moe::kRouterFusedMaxTokens;
+  const size_t lds = (size_t)E * sizeof(int);
+  if (a.V <= 8)
+    launch_router_v<8>(k, fused, (int)T, lds, stream, a);
+  else if (a.V <= 16)
+    launch_router_v<16>(k, fused, (int)T, lds, stream, a);
+  else if (a.V <= 32)
+    launch_router_v<32>(k, fused, (int)T, lds, stream, a);
+  else
+    launch_router_v<64>(k, fused, (int)T, lds, stream, a);
   return last_launch_status();
 }
 

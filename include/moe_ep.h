@@ -110,6 +110,45 @@ moe_status moe_get_dispatch_layout(const moe_shape* shape, const int32_t* topk_i
                                    uint8_t* is_token_in_rank, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+/* Gate of a router fused with the layout (moe_route_layout). */
+typedef enum moe_gate {
+  MOE_GATE_SOFTMAX = 0, /* w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected */
+  MOE_GATE_SIGMOID = 1  /* w_j = s(l_j) / sum_i s(l_i), s(x) = 1 / (1 + exp(-x)), over the k selected */
+} moe_gate;
+
+typedef struct moe_router {
+  int32_t gate;        /* moe_gate */
+  int32_t num_groups;  /* G: experts form G equal contiguous groups; 1 = no group limit */
+  int32_t topk_groups; /* groups kept per token, 1 <= topk_groups <= G */
+} moe_router;
+
+/* Top-k gating fused with the dispatch layout.  [overlap notes, 节点内通信: top-k
+ * runs together with the sparse exchange, no CPU step between them; section
+ * 计算-通信重叠: DeepSeek's group-limited gating.]
+ *
+ * Per token: with G > 1, each group is scored by its largest logit and the
+ * topk_groups best groups are kept (equal scores: the lower group first); the k
+ * largest logits among the kept groups' experts are selected, equal logits in
+ * ascending id order (-0.0 equals +0.0), and written in descending order of
+ * logit; the weights follow `gate` in fp32.  Then everything
+ * moe_get_dispatch_layout computes is computed from those ids, so moe_dispatch
+ * can follow directly.
+ *
+ *   router            in  gate, num_groups, topk_groups
+ *   logits            in  float[T, E]     finite router logits (NaN: selection unspecified)
+ *   topk_idx          out int32[T, k]     selected expert ids, slot order
+ *   topk_w            out float[T, k]     gate weights
+ *   tokens_per_rank, tokens_per_expert, is_token_in_rank, workspace: as moe_get_dispatch_layout
+ *
+ * Limits: E % 8 == 0 and E <= 512, k <= 16, num_groups in {1, 2, 4, 8}
+ * (MOE_ERR_UNSUPPORTED otherwise); E % num_groups == 0 and
+ * k <= topk_groups * E / num_groups (MOE_ERR_INVALID_ARG otherwise).
+ */
+moe_status moe_route_layout(const moe_shape* shape, const moe_router* router, const float* logits,
+                            int32_t* topk_idx, float* topk_w, int32_t* tokens_per_rank,
+                            int32_t* tokens_per_expert, uint8_t* is_token_in_rank, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
 /* Dispatch.  [overlap notes, 节点内通信: filtered send, FP8 transport;
  * rocSHMEM notes 3.2: rows packed into a preallocated receive buffer.]
  *

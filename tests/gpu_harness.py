@@ -109,3 +109,44 @@ def run_combine_ll(shape, y: np.ndarray, idx_d: torch.Tensor, w: np.ndarray, slo
     moe.moe_combine_ll(shape, yd, idx_d, w_d, slot_pos_d, out)
     torch.cuda.synchronize()
     return bf16_to_np(out)
+
+
+def run_route(logits: np.ndarray, k: int, E: int, R: int, gate: str = "softmax", num_groups: int = 1,
+              topk_groups: int = 1, misalign: bool = False, H: int = 128) -> PathResult:
+    """moe_route_layout on fp32 logits [T, E]; with ``misalign`` the logits start 4 bytes past a
+    16-byte boundary (the scalar-load path)."""
+    T = logits.shape[0]
+    shape = moe.MoeShape(T, H, k, E, R)
+    flat = np.ascontiguousarray(logits, dtype=np.float32).reshape(-1)
+    if misalign:
+        buf = torch.empty(flat.size + 4, dtype=torch.float32, device="cuda")
+        buf[1:1 + flat.size].copy_(torch.from_numpy(flat))
+        ld = buf[1:1 + flat.size].view(T, E)
+    else:
+        ld = torch.from_numpy(flat).cuda().view(T, E)
+    lay = moe.alloc_route(shape)
+    _poison(lay)
+    moe.run_route(shape, ld, lay, gate, num_groups, topk_groups)
+    torch.cuda.synchronize()
+    r = PathResult()
+    r["shape"] = shape
+    for key in ("topk_idx", "topk_w", "tokens_per_rank", "tokens_per_expert", "is_token_in_rank"):
+        r[key] = lay[key].cpu().numpy()
+    r["_dev"] = {"logits": ld, "lay": lay}
+    return r
+
+
+def dispatch_with_plan(res: PathResult, x: np.ndarray, dtype: str = "bf16") -> PathResult:
+    """moe_dispatch of x with the ids, weights and plan moe_route_layout produced."""
+    shape = res["shape"]
+    lay = res["_dev"]["lay"]
+    xd = to_dev_bf16(x) if shape.num_tokens else torch.empty((0, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    d = moe.alloc_dispatch(shape, dtype)
+    _poison(d)
+    moe.run_dispatch(shape, dtype, xd, lay["topk_idx"], lay["topk_w"], lay, d)
+    torch.cuda.synchronize()
+    out = PathResult()
+    for key in ("recv_src_idx", "recv_topk_idx", "recv_topk_w", "rank_offsets", "send_row", "num_recv"):
+        out[key] = d[key].cpu().numpy()
+    out["recv_x"] = bf16_to_np(d["recv_x"]) if dtype == "bf16" else d["recv_x"].cpu().numpy()
+    return out

@@ -132,3 +132,34 @@ def test_binding_rejects_host_tensors():
         L.moe_combine(s, torch.zeros(8, 256, dtype=torch.bfloat16), torch.zeros(4, 2, dtype=torch.int32),
                       torch.zeros(4, 2), torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 256, dtype=torch.bfloat16),
                       stream=0)
+
+
+def route(s, gate=0, G=1, KG=1, router=True, logits=A, idx=A, w=A, tpr=A, tpe=A, mask=A, ws=A, ws_bytes=1 << 30):
+    r = L.MoeRouterC(gate, G, KG)
+    return L.lib.moe_route_layout(ctypes.byref(s), ctypes.byref(r) if router else None, logits, idx, w, tpr, tpe,
+                                  mask, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,shape_kw,code", [
+    (dict(router=False), {}, INVALID),
+    (dict(gate=2), {}, INVALID),
+    (dict(gate=-1), {}, INVALID),
+    (dict(G=0), {}, INVALID),
+    (dict(G=4, KG=5), {}, INVALID),
+    (dict(G=4, KG=0), {}, INVALID),
+    (dict(G=3, KG=1), dict(E=24, R=4), UNSUPPORTED),      # groups must be 1, 2, 4 or 8
+    (dict(G=16, KG=2), dict(E=64, R=4), UNSUPPORTED),
+    (dict(G=8, KG=1), dict(E=16, k=4, R=4), INVALID),      # k > topk_groups * E / G = 2
+    (dict(), dict(E=12, R=4, k=4), UNSUPPORTED),           # E % 8 != 0
+    (dict(), dict(E=1024, R=8, k=8), UNSUPPORTED),         # E > 512
+    (dict(), dict(E=64, R=8, k=17), UNSUPPORTED),          # k > 16
+    (dict(logits=0), {}, INVALID),
+    (dict(idx=0), {}, INVALID),
+    (dict(w=0), {}, INVALID),
+    (dict(tpr=0), {}, INVALID),
+    (dict(ws=A + 64), {}, INVALID),                        # workspace not 256-byte aligned
+    (dict(ws_bytes=16), {}, INVALID),
+    (dict(logits=A + 2), {}, INVALID),
+])
+def test_route_layout_rejects(kw, shape_kw, code):
+    assert route(shape(**shape_kw), **kw) == code
