@@ -10,18 +10,20 @@
 //     descending order;
 //   * weights: softmax over the k selected logits, or the sigmoid gate
 //     normalised over the k selected (fp32, expf);
-// and, in the same pass, what the layout kernels compute from the ids: the
-// token's rank bitmask and is_token_in_rank row, per-64-token-chunk rank counts
-// and per-block expert histograms.
+// and what the layout kernels compute from the ids: the token's rank bitmask
+// and is_token_in_rank row, per-64-token-chunk rank counts and per-chunk expert
+// histograms (router_count_kernel; layout_finalize_kernel follows).  For small
+// batches the router runs on one wave per 8 tokens to spread over many CUs and
+// layout_fused_kernel follows (router_tokens_kernel).
 //
 // Work split: 8 lanes per token, lane p holding experts [p*V, p*V + V),
-// V = E / 8, so a wave routes 8 tokens and a block of 8 waves one 64-token
-// layout chunk.  Each lane sorts its V candidates into a register list of the
-// best KL (insertion with a constant per-position comparison, so equal logits
-// keep the earlier, lower id); the token's k picks are then k rounds of a max
-// over the 8 list heads, keyed by (logit, lower id), whose owner pops its head.
-// Logits are compared through an order-preserving unsigned key (-0.0 folded
-// into +0.0), so every selection decision is exact.
+// V = E / 8.  Candidates are ordered by (logit key, then lower expert id).
+// Each lane keeps a sorted register list of its KL best; the token's k picks
+// are k rounds of a max over the 8 list heads (DPP lane exchanges, 32-bit
+// operations only: 64-bit compares cost several times more on this GPU) whose
+// owner pops its head.  A lane that runs out of list entries while picks
+// remain rebuilds its list from the candidates after its last pick
+// ("refill"), so KL bounds only the work, not k.
 #pragma once
 
 #include "device_common.h"
@@ -29,11 +31,10 @@
 
 namespace moe {
 
-constexpr int kRouterLanes = 8;                           // lanes per token
+constexpr int kRouterLanes = 8;                             // lanes per token
 constexpr int kRouterTokensPerWave = kWave / kRouterLanes;  // 8
-constexpr int kRouterBlock = 512;                         // 8 waves = one 64-token chunk
-constexpr int kRouterFusedMaxTokens = 128;                // one block of up to 16 waves does all
-constexpr int kRouterMaxExperts = 512;                    // V <= 64
+constexpr int kRouterBlock = 512;                           // 8 waves = one 64-token chunk
+constexpr int kRouterList = 4;                              // KL: list entries per lane
 
 struct RouterArgs {
   const float* logits;  // [T, E]
@@ -61,65 +62,151 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Routes tokens t0 + (lane >> 3); returns the token's rank bitmask (same in its
-// 8 lanes; 0 for t >= T) and adds its experts to the LDS histogram.
-template <int VMAX, int KL>
-__device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int lane, int* hist) {
+// Lane exchanges inside aligned groups of 8 lanes (DPP, no LDS round trip):
+// kXor1 / kXor2 swap neighbours / pairs within a quad, kMirror8 maps lane i of
+// a half row to lane 7 - i.  After kXor1 and kXor2 every lane of a quad holds
+// the quad's result, so kMirror8 then combines the two quads.
+constexpr int kXor1 = 0xb1;      // quad_perm [1, 0, 3, 2]
+constexpr int kXor2 = 0x4e;      // quad_perm [2, 3, 0, 1]
+constexpr int kMirror8 = 0x141;  // row_half_mirror
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, 0xf, 0xf, false);
+}
+
+// Max over the 8 lanes of (key, n) pairs ordered by key, then n (n = ~id:
+// the lower id wins a tie).  32-bit operations only.
+template <int kCtrl>
+__device__ __forceinline__ void pair_max_step(uint32_t& k, uint32_t& n) {
+  const uint32_t ok = dpp32<kCtrl>(k), on = dpp32<kCtrl>(n);
+  const bool take = ok > k || (ok == k && on > n);
+  k = take ? ok : k;
+  n = take ? on : n;
+}
+
+__device__ __forceinline__ void max8_pair(uint32_t& k, uint32_t& n) {
+  pair_max_step<kXor1>(k, n);
+  pair_max_step<kXor2>(k, n);
+  pair_max_step<kMirror8>(k, n);
+}
+
+__device__ __forceinline__ uint32_t or8_u32(uint32_t x) {
+  x |= dpp32<kXor1>(x);
+  x |= dpp32<kXor2>(x);
+  return x | dpp32<kMirror8>(x);
+}
+
+// The same value in all 8 lanes: ((a0 + a1) + (a2 + a3)) + ((a4 + a5) + (a6 + a7)),
+// up to the order of operands of each addition, which does not change a sum.
+__device__ __forceinline__ float sum8_f32(float x) {
+  x = x + __uint_as_float(dpp32<kXor1>(__float_as_uint(x)));
+  x = x + __uint_as_float(dpp32<kXor2>(__float_as_uint(x)));
+  return x + __uint_as_float(dpp32<kMirror8>(__float_as_uint(x)));
+}
+
+// A lane's list: its best candidates, keys descending (0 = empty), with their
+// expert ids.  Candidates are offered in ascending id order, so a new one loses
+// every tie with an entry already listed and `key > lk[i]` alone decides where
+// it goes; entries below the insertion point shift down, the last falls off.
+// Keys move with min / max; ids with bitwise selects on all-ones / zero masks.
+// The empty asm hides the masks from the optimiser, which would otherwise turn
+// the nested selects into branches.
+__device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
+template <int KL>
+__device__ __forceinline__ void list_insert(uint32_t (&lk)[KL], int (&li)[KL], uint32_t key, int id) {
+  uint32_t gt[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) {
+    gt[i] = key > lk[i] ? ~0u : 0u;  // all ones from the insertion point on
+    __asm__("" : "+v"(gt[i]));
+  }
+#pragma unroll
+  for (int i = KL - 1; i > 0; --i) {
+    li[i] = (int)bitsel(gt[i], bitsel(gt[i - 1], (uint32_t)li[i - 1], (uint32_t)id), (uint32_t)li[i]);
+    lk[i] = max(lk[i], min(key, lk[i - 1]));
+  }
+  li[0] = (int)bitsel(gt[0], (uint32_t)id, (uint32_t)li[0]);
+  lk[0] = max(lk[0], key);
+}
+
+// Offers the lane's V candidates (ids id0 + v) to the list: all of them, or
+// with `refill`, only those ordered after the lane's last pick (fk, fid).  A
+// rolled loop keeps the code small; the load two 16-byte chunks ahead is
+// issued before the current chunk is inserted (the empty asm keeps the
+// compiler from sinking it).  `row` must be readable for V values.
+template <int KL>
+__device__ __forceinline__ void list_fill(uint32_t (&lk)[KL], int (&li)[KL], const float* row, int V, bool vec4,
+                                          int id0, bool live, bool refill, uint32_t fk, int fid) {
+  auto offer = [&](uint32_t u, int v) {
+    uint32_t key = live ? logit_key(u) : 0u;
+    const int id = id0 + v;
+    if (refill) key = (key < fk || (key == fk && id > fid)) ? key : 0u;
+    list_insert<KL>(lk, li, key, id);
+  };
+  if (vec4) {
+    const u32x4* r4 = reinterpret_cast<const u32x4*>(row);
+    const int n4 = V >> 2;
+    u32x4 c0 = r4[0];
+    u32x4 c1 = r4[min(1, n4 - 1)];
+#pragma unroll 1
+    for (int c = 0; c < n4; ++c) {
+      const u32x4 cur = c0;
+      c0 = c1;
+      c1 = r4[min(c + 2, n4 - 1)];
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 4; ++i) offer(cur[i], 4 * c + i);
+    }
+  } else {
+    const uint32_t* r1 = reinterpret_cast<const uint32_t*>(row);
+    uint32_t c0 = r1[0];
+    uint32_t c1 = r1[min(1, V - 1)];
+#pragma unroll 1
+    for (int v = 0; v < V; ++v) {
+      const uint32_t cur = c0;
+      c0 = c1;
+      c1 = r1[min(v + 2, V - 1)];
+      __asm__ volatile("" ::: "memory");
+      offer(cur, v);
+    }
+  }
+}
+
+// Routes token t with the 8 lanes of its lane group: writes its ids and
+// weights; returns its rank bitmask (same in the 8 lanes; 0 for t >= T) and
+// the expert ids of the lane's slots j = q * 8 + p in `sel` (-1: none).
+template <int KS>
+__device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int lane, int (&sel)[KS]) {
 #pragma clang fp contract(off)
+  constexpr int KL = kRouterList;
   const LayoutArgs& L = a.lay;
   const int p = lane & (kRouterLanes - 1);
   const int gbase = lane & ~(kRouterLanes - 1);
   const bool live = t < L.T;
 
-  // 1. this lane's V logits as bits (all loads issued before any is used);
-  //    kNoLogit beyond V or for t >= T, so the sort below needs no conditions
-  uint32_t xb[VMAX];
-  const float* row = a.logits + (size_t)min(t, max(L.T - 1, 0)) * L.E + (size_t)p * a.V;
-  if (a.vec4) {
-#pragma unroll
-    for (int v = 0; v < VMAX; v += 4) {
-      u32x4 q = {kNoLogit, kNoLogit, kNoLogit, kNoLogit};
-      if (live && v < a.V) q = *reinterpret_cast<const u32x4*>(row + v);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xb[v + i] = q[i];
-    }
-  } else {
-    const uint32_t* rowb = reinterpret_cast<const uint32_t*>(row);
-#pragma unroll
-    for (int v = 0; v < VMAX; ++v) xb[v] = live && v < a.V ? rowb[v] : kNoLogit;
-  }
-
-  // 2. per-lane sorted list of the best KL candidates.  Positions v ascend
-  //    with the expert id, so a strict comparison keeps equal logits in id order.
+  // 1-2. the lane's best KL candidates (rows t >= T read row T - 1 and offer nothing)
+  const float* row = a.logits + (size_t)min(t, L.T - 1) * L.E + (size_t)p * a.V;
+  const int id0 = p * a.V;
   uint32_t lk[KL];
-  int li[KL];  // position v within the lane (a constant per insertion), expert = p * V + v
+  int li[KL];
 #pragma unroll
   for (int i = 0; i < KL; ++i) {
     lk[i] = 0u;
     li[i] = 0;
   }
-#pragma unroll
-  for (int v = 0; v < VMAX; ++v) {
-    const uint32_t nk = logit_key(xb[v]);
-    bool c[KL];
-#pragma unroll
-    for (int i = 0; i < KL; ++i) c[i] = nk > lk[i];  // true from the insertion point on
-#pragma unroll
-    for (int i = KL - 1; i > 0; --i) {
-      lk[i] = c[i] ? (c[i - 1] ? lk[i - 1] : nk) : lk[i];
-      li[i] = c[i] ? (c[i - 1] ? li[i - 1] : v) : li[i];
-    }
-    lk[0] = c[0] ? nk : lk[0];
-    li[0] = c[0] ? v : li[0];
-  }
+  list_fill<KL>(lk, li, row, a.V, a.vec4 != 0, id0, live, false, 0u, 0);
+  bool exhausted = lk[0] == 0u;
 
   // 3. group-limited gating: 8 / G consecutive lanes form one group, so the
-  //    group score is the largest list head among them; a lane of a group that
-  //    is not kept empties its list.
+  //    group score is the largest list head among them; lanes of groups that
+  //    are not kept empty their lists.
   if (a.G > 1) {
     const int lpg = kRouterLanes / a.G;
     uint32_t m = lk[0];
-    for (int s = 1; s < lpg; s <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s, kWave));
+    if (lpg >= 2) m = max(m, dpp32<kXor1>(m));
+    if (lpg >= 4) m = max(m, dpp32<kXor2>(m));
     const int g = p / lpg;
     int better = 0;
     for (int q = 0; q < a.G; ++q) {
@@ -129,95 +216,92 @@ __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int 
     if (better >= a.KG) {
 #pragma unroll
       for (int i = 0; i < KL; ++i) lk[i] = 0u;
+      exhausted = true;
     }
   }
 
   // 4. k rounds over the 8 heads; slot j is kept by lane j % 8
-  constexpr int kSlots = KL / kRouterLanes;  // slots per lane (k <= KL)
-  int sid[kSlots];
-  uint32_t skey[kSlots];
+  uint32_t skey[KS];
 #pragma unroll
-  for (int q = 0; q < kSlots; ++q) {
-    sid[q] = -1;
+  for (int q = 0; q < KS; ++q) {
+    sel[q] = -1;
     skey[q] = 0u;
   }
-  uint64_t ranks = 0;
-  uint32_t key0 = 0u;
+  uint32_t key0 = 0u, fk = 0u;
+  int fid = 0;
   for (int j = 0; j < L.k; ++j) {
-    const uint64_t mine = ((uint64_t)lk[0] << 32) | (uint32_t)~(p * a.V + li[0]);
-    uint64_t best = mine;
-#pragma unroll
-    for (int s = 1; s < kRouterLanes; s <<= 1) {
-      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, s, kWave);
-      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), s, kWave);
-      const uint64_t o = ((uint64_t)hi << 32) | lo;
-      best = o > best ? o : best;
-    }
-    const int id = (int)~(uint32_t)best;
-    const uint32_t bk = (uint32_t)(best >> 32);
+    uint32_t bk = lk[0], bn = ~(uint32_t)li[0];
+    max8_pair(bk, bn);
+    const int id = (int)~bn;
     if (j == 0) key0 = bk;
-    ranks |= 1ull << rank_of(id, L.rank_magic);
 #pragma unroll
-    for (int q = 0; q < kSlots; ++q) {  // no dynamic register indexing
+    for (int q = 0; q < KS; ++q) {  // no dynamic register indexing
       if (j == q * kRouterLanes + p) {
-        sid[q] = id;
+        sel[q] = id;
         skey[q] = bk;
       }
     }
-    if (best == mine) {  // the owner pops its head
+    if (lk[0] == bk && li[0] == id) {  // the owner pops its head
+      fk = bk;
+      fid = id;
 #pragma unroll
       for (int i = 0; i + 1 < KL; ++i) {
         lk[i] = lk[i + 1];
         li[i] = li[i + 1];
       }
       lk[KL - 1] = 0u;
-      li[KL - 1] = 0;
+    }
+    if (j >= KL - 1 && j + 1 < L.k) {  // a lane can run dry only after KL pops
+      const bool need = !exhausted && lk[0] == 0u;
+      if (__ballot(need)) {  // rare: a lane gave all KL of its entries
+        if (need) list_fill<KL>(lk, li, row, a.V, a.vec4 != 0, id0, live, true, fk, fid);
+        exhausted = exhausted || (need && lk[0] == 0u);
+      }
     }
   }
 
-  // 5. weights, summed in a fixed order (per lane, then a butterfly over the 8 lanes)
-  float ev[kSlots];
+  // 5. weights, summed in a fixed order (per lane, then over the 8 lanes), and
+  //    the rank bitmask
+  float ev[KS];
   float sum = 0.0f;
+  uint32_t rlo = 0u, rhi = 0u;
 #pragma unroll
-  for (int q = 0; q < kSlots; ++q) {
-    const float l = key_logit(skey[q]);
-    float e = a.sigmoid ? 1.0f / (1.0f + expf(-l)) : expf(l - key_logit(key0));
-    e = sid[q] >= 0 ? e : 0.0f;
+  for (int q = 0; q < KS; ++q) {
+    const float lg = key_logit(skey[q]);
+    float e = a.sigmoid ? 1.0f / (1.0f + expf(-lg)) : expf(lg - key_logit(key0));
+    e = sel[q] >= 0 ? e : 0.0f;
     ev[q] = e;
     sum = sum + e;
+    if (sel[q] >= 0) {
+      const int r = rank_of(sel[q], L.rank_magic) & 63;  // (ids of rows t >= T are discarded)
+      rlo |= r < 32 ? 1u << r : 0u;
+      rhi |= r >= 32 ? 1u << (r - 32) : 0u;
+    }
   }
-#pragma unroll
-  for (int s = 1; s < kRouterLanes; s <<= 1) sum = sum + __shfl_xor(sum, s, kWave);
+  sum = sum8_f32(sum);
+  const uint64_t ranks = ((uint64_t)or8_u32(rhi) << 32) | or8_u32(rlo);
 
   if (live) {
 #pragma unroll
-    for (int q = 0; q < kSlots; ++q) {
+    for (int q = 0; q < KS; ++q) {
       const int j = q * kRouterLanes + p;
       if (j < L.k) {
-        a.topk_idx[(size_t)t * L.k + j] = sid[q];
+        a.topk_idx[(size_t)t * L.k + j] = sel[q];
         a.topk_w[(size_t)t * L.k + j] = ev[q] / sum;
-        atomicAdd(&hist[sid[q]], 1);
       }
     }
-    // layout outputs of this token: bitmask and is_token_in_rank row
-    if (p == 0) L.token_ranks[t] = ranks;
-    uint8_t* dst = L.mask + (size_t)t * L.R;
-    if (L.mask_words) {
-      uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
-      for (int w = p; w < (L.R >> 2); w += kRouterLanes) {
-        const uint32_t b = (uint32_t)(ranks >> (4 * w)) & 0xfu;
-        d32[w] = (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
-      }
-    } else {
-      for (int r = p; r < L.R; r += kRouterLanes) dst[r] = (uint8_t)((ranks >> r) & 1u);
-    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < KS; ++q) sel[q] = -1;
   }
   return live ? ranks : 0;
 }
 
-// T > kRouterFusedMaxTokens: block b routes chunk b (64 tokens) and writes its
-// chunk counts and expert histogram; layout_finalize_kernel (NB = NC) follows.
-template <int VMAX, int KL>
+// T > kFusedMaxTokens (so T >= 1): block b routes chunk b (64 tokens, 8 per wave) and
+// writes everything layout_count_kernel writes for it (rank bitmasks, mask
+// rows, chunk counts, an expert histogram row); layout_finalize_kernel (with
+// NB = number of chunks) completes the layout.
+template <int KS>
 __global__ __launch_bounds__(kRouterBlock) void router_count_kernel(RouterArgs a) {
   extern __shared__ int hist[];  // [E]
   __shared__ uint64_t chunk_masks[kWave];
@@ -227,8 +311,27 @@ __global__ __launch_bounds__(kRouterBlock) void router_count_kernel(RouterArgs a
   __syncthreads();
 
   const int tw = wave * kRouterTokensPerWave + (lane >> 3);  // token within the chunk
-  const uint64_t m = route_token<VMAX, KL>(a, blockIdx.x * kWave + tw, lane, hist);
-  if ((lane & (kRouterLanes - 1)) == 0) chunk_masks[tw] = m;
+  const int t = blockIdx.x * kWave + tw;
+  const int p = lane & (kRouterLanes - 1);
+  int sel[KS];
+  const uint64_t m = route_token<KS>(a, t, lane, sel);
+#pragma unroll
+  for (int q = 0; q < KS; ++q)
+    if (sel[q] >= 0) atomicAdd(&hist[sel[q]], 1);
+  if (t < L.T) {
+    if (p == 0) L.token_ranks[t] = m;
+    uint8_t* dst = L.mask + (size_t)t * L.R;
+    if (L.mask_words) {
+      uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+      for (int w = p; w < (L.R >> 2); w += kRouterLanes) {
+        const uint32_t b = (uint32_t)(m >> (4 * w)) & 0xfu;
+        d32[w] = (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
+      }
+    } else {
+      for (int r = p; r < L.R; r += kRouterLanes) dst[r] = (uint8_t)((m >> r) & 1u);
+    }
+  }
+  if (p == 0) chunk_masks[tw] = m;
   __syncthreads();
 
   if (wave == 0) {
@@ -238,45 +341,13 @@ __global__ __launch_bounds__(kRouterBlock) void router_count_kernel(RouterArgs a
   for (int e = tid; e < L.E; e += kRouterBlock) L.block_expert[(size_t)blockIdx.x * L.E + e] = hist[e];
 }
 
-// T <= kRouterFusedMaxTokens: one block of ceil(T / 8) waves (at least one)
-// routes every token and finishes the layout (at most two chunks).
-template <int VMAX, int KL>
-__global__ __launch_bounds__(kRouterFusedMaxTokens * kRouterLanes) void router_layout_fused_kernel(RouterArgs a) {
-  extern __shared__ int hist[];  // [E]
-  __shared__ uint64_t masks[kRouterFusedMaxTokens];
-  __shared__ int chunk_cnt[2][kWave];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const LayoutArgs& L = a.lay;
-  for (int e = tid; e < L.E; e += blockDim.x) hist[e] = 0;
-  for (int i = tid; i < kRouterFusedMaxTokens; i += blockDim.x) masks[i] = 0;
-  __syncthreads();
-
-  const int t = wave * kRouterTokensPerWave + (lane >> 3);
-  const uint64_t m = route_token<VMAX, KL>(a, t, lane, hist);
-  if ((lane & (kRouterLanes - 1)) == 0 && t < kRouterFusedMaxTokens) masks[t] = m;
-  __syncthreads();
-
-  if (wave < 2) {  // chunk `wave`: per-rank token counts
-    const int cnt = wave_rank_counts(masks[wave * kWave + lane], L.R, lane);
-    if (lane < L.R) chunk_cnt[wave][lane] = cnt;
-  }
-  for (int e = tid; e < L.E; e += blockDim.x) L.tokens_per_expert[e] = hist[e];
-  __syncthreads();
-  if (wave == 0) {
-    int c0 = 0, total = 0;
-    if (lane < L.R) {
-      c0 = chunk_cnt[0][lane];
-      total = c0 + (L.NC > 1 ? chunk_cnt[1][lane] : 0);
-      if (L.NC > 0) L.chunk_base[lane * L.NC] = 0;
-      if (L.NC > 1) L.chunk_base[lane * L.NC + 1] = c0;
-    }
-    const int incl = wave_inclusive_scan(lane < L.R ? total : 0, lane);
-    if (lane < L.R) {
-      L.tokens_per_rank[lane] = total;
-      L.ws_rank_offsets[lane] = incl - total;
-    }
-    if (lane == L.R - 1) L.ws_rank_offsets[L.R] = incl;
-  }
+// 1 <= T <= kFusedMaxTokens: one wave per 8 tokens, ids and weights only;
+// layout_fused_kernel follows on the ids.
+template <int KS>
+__global__ __launch_bounds__(kWave) void router_tokens_kernel(RouterArgs a) {
+  const int lane = threadIdx.x;
+  int sel[KS];
+  route_token<KS>(a, blockIdx.x * kRouterTokensPerWave + (lane >> 3), lane, sel);
 }
 
 }  // namespace moe

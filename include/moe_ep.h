@@ -140,7 +140,7 @@ typedef struct moe_router {
  *   topk_w            out float[T, k]     gate weights
  *   tokens_per_rank, tokens_per_expert, is_token_in_rank, workspace: as moe_get_dispatch_layout
  *
- * Limits: E % 8 == 0 and E <= 512, k <= 16, num_groups in {1, 2, 4, 8}
+ * Limits: E % 8 == 0, k <= 16, num_groups in {1, 2, 4, 8}
  * (MOE_ERR_UNSUPPORTED otherwise); E % num_groups == 0 and
  * k <= topk_groups * E / num_groups (MOE_ERR_INVALID_ARG otherwise).
  */

@@ -151,7 +151,7 @@ def route(s, gate=0, G=1, KG=1, router=True, logits=A, idx=A, w=A, tpr=A, tpe=A,
     (dict(G=16, KG=2), dict(E=64, R=4), UNSUPPORTED),
     (dict(G=8, KG=1), dict(E=16, k=4, R=4), INVALID),      # k > topk_groups * E / G = 2
     (dict(), dict(E=12, R=4, k=4), UNSUPPORTED),           # E % 8 != 0
-    (dict(), dict(E=1024, R=8, k=8), UNSUPPORTED),         # E > 512
+    (dict(), dict(E=4104, R=8, k=8), UNSUPPORTED),         # E above the library limit
     (dict(), dict(E=64, R=8, k=17), UNSUPPORTED),          # k > 16
     (dict(logits=0), {}, INVALID),
     (dict(idx=0), {}, INVALID),

@@ -115,6 +115,8 @@ EDGES = [  # (label, T, E, k, R, gate, G, KG, ties, misalign)
     ("E = 264 (V = 33)", 96, 264, 7, 8, "softmax", 1, 1, True, False),
     ("one group kept of 8", 500, 256, 8, 32, "softmax", 8, 1, True, False),
     ("R = 64", 1000, 256, 8, 64, "softmax", 8, 4, False, False),
+    ("E = 1024", 300, 1024, 8, 16, "softmax", 8, 4, True, False),
+    ("E = 4096, multi-block", 1100, 4096, 16, 64, "sigmoid", 4, 2, False, False),
 ]
 
 
