@@ -220,17 +220,18 @@ void launch_ll_dispatch(int U, dim3 grid, hipStream_t stream, const moe::LlDispa
 }
 
 
-template <int KS>
+template <int P, int KS>
 void launch_router(int T, size_t lds, hipStream_t stream, const moe::RouterArgs& a) {
   if (T <= moe::kFusedMaxTokens) {  // many one-wave blocks, then the one-block layout on the ids
     if (T > 0) {
-      const int blocks = (T + moe::kRouterTokensPerWave - 1) / moe::kRouterTokensPerWave;
-      hipLaunchKernelGGL((moe::router_tokens_kernel<KS>), dim3(blocks), dim3(moe::kWave), 0, stream, a);
+      constexpr int tokens_per_wave = moe::kWave / P;
+      const int blocks = (T + tokens_per_wave - 1) / tokens_per_wave;
+      hipLaunchKernelGGL((moe::router_tokens_kernel<P, KS>), dim3(blocks), dim3(moe::kWave), 0, stream, a);
     }
     const int threads = std::max(moe::kWave, (T + moe::kWave - 1) / moe::kWave * moe::kWave);
     hipLaunchKernelGGL(moe::layout_fused_kernel, dim3(1), dim3(threads), lds, stream, a.lay);
   } else {
-    hipLaunchKernelGGL((moe::router_count_kernel<KS>), dim3(a.lay.NC), dim3(moe::kRouterBlock), lds, stream, a);
+    hipLaunchKernelGGL((moe::router_count_kernel<P, KS>), dim3(a.lay.NC), dim3(moe::kWave * P), lds, stream, a);
     hipLaunchKernelGGL(moe::layout_finalize_kernel, dim3(1), dim3(1024), 0, stream, a.lay);
   }
 }
@@ -321,7 +322,7 @@ moe_status moe_route_layout(const moe_shape* shape, const moe_router* router, co
   const int E = s.num_experts, k = s.num_topk, G = router->num_groups, KG = router->topk_groups;
   if (router->gate != MOE_GATE_SOFTMAX && router->gate != MOE_GATE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (G < 1 || KG < 1 || KG > G) return MOE_ERR_INVALID_ARG;
-  if (E % 8 != 0 || k > 16) return MOE_ERR_UNSUPPORTED;
+  if (E % 8 != 0 || k > moe::kRouterMaxK) return MOE_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8) return MOE_ERR_UNSUPPORTED;
   if (E % G != 0 || k > KG * (E / G)) return MOE_ERR_INVALID_ARG;
   if (!present(logits, T) || !present(topk_idx, T) || !present(topk_w, T) || !present(is_token_in_rank, T) ||
@@ -355,17 +356,19 @@ moe_status moe_route_layout(const moe_shape* shape, const moe_router* router, co
   a.lay.NB = p.NC;  // one expert histogram row per routed 64-token chunk
   a.lay.mask_words = (s.num_ranks % 4 == 0 && aligned(is_token_in_rank, 4)) ? 1 : 0;
   a.lay.ids_vec4 = (k % 4 == 0 && aligned(topk_idx, 16)) ? 1 : 0;  // the layout kernel's reads of the ids
-  a.V = E / 8;
+  a.V = E % 16 == 0 ? E / 16 : E / 8;  // experts per lane: 16 or 8 lanes per token
   a.G = G;
   a.KG = KG;
   a.sigmoid = router->gate == MOE_GATE_SIGMOID ? 1 : 0;
   a.vec4 = (a.V % 4 == 0 && aligned(logits, 16)) ? 1 : 0;
 
   const size_t lds = (size_t)E * sizeof(int);
-  if (k <= moe::kRouterTokensPerWave)
-    launch_router<1>((int)T, lds, stream, a);
+  if (E % 16 == 0)  // 16 lanes per token, one slot per lane
+    launch_router<16, 1>((int)T, lds, stream, a);
+  else if (k <= 8)
+    launch_router<8, 1>((int)T, lds, stream, a);
   else
-    launch_router<2>((int)T, lds, stream, a);
+    launch_router<8, 2>((int)T, lds, stream, a);
   return last_launch_status();
 }
 

@@ -13,13 +13,13 @@
 // and what the layout kernels compute from the ids: the token's rank bitmask
 // and is_token_in_rank row, per-64-token-chunk rank counts and per-chunk expert
 // histograms (router_count_kernel; layout_finalize_kernel follows).  For small
-// batches the router runs on one wave per 8 tokens to spread over many CUs and
-// layout_fused_kernel follows (router_tokens_kernel).
+// batches the router runs on one wave per 64 / P tokens to spread over many
+// CUs and layout_fused_kernel follows (router_tokens_kernel).
 //
-// Work split: 8 lanes per token, lane p holding experts [p*V, p*V + V),
-// V = E / 8.  Candidates are ordered by (logit key, then lower expert id).
+// Work split: P lanes per token (16 when E % 16 == 0, else 8), lane p
+// holding experts [p*V, p*V + V), V = E / P.  Candidates are ordered by (logit key, then lower expert id).
 // Each lane keeps a sorted register list of its KL best; the token's k picks
-// are k rounds of a max over the 8 list heads (DPP lane exchanges, 32-bit
+// are k rounds of a max over the P list heads (DPP lane exchanges, 32-bit
 // operations only: 64-bit compares cost several times more on this GPU) whose
 // owner pops its head.  A lane that runs out of list entries while picks
 // remain rebuilds its list from the candidates after its last pick
@@ -31,78 +31,87 @@
 
 namespace moe {
 
-constexpr int kRouterLanes = 8;                             // lanes per token
-constexpr int kRouterTokensPerWave = kWave / kRouterLanes;  // 8
-constexpr int kRouterBlock = 512;                           // 8 waves = one 64-token chunk
-constexpr int kRouterList = 4;                              // KL: list entries per lane
+constexpr int kRouterList = 4;  // KL: list entries per lane
+constexpr int kRouterMaxK = 16;  // slots per token handled (one or two per lane)
 
 struct RouterArgs {
   const float* logits;  // [T, E]
   int32_t* topk_idx;    // [T, k]
   float* topk_w;        // [T, k]
   LayoutArgs lay;       // outputs and plan, as the layout kernels fill them
-  int V;                // experts per lane, E / 8
+  int V;                // experts per lane, E / P
   int G, KG;            // groups, kept groups (G = 1: no group limit)
   int sigmoid;          // 0: softmax over the selected, 1: normalised sigmoid
   int vec4;             // 1: logit rows read as 16-byte vectors
 };
 
-// Order-preserving map of fp32 bits to uint32 (larger float, larger key),
-// with -0.0 folded into +0.0.  Finite and infinite logits map to keys
-// >= 0x007fffff; the bit pattern 0xffffffff (a NaN, never a valid logit) maps
-// to 0, which marks "not eligible".
-constexpr uint32_t kNoLogit = 0xffffffffu;
-
-__device__ __forceinline__ uint32_t logit_key(uint32_t u) {
-  u = u == 0x80000000u ? 0u : u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+// Order-preserving map fp32 -> uint32 (larger float, larger key).  x + 0.0
+// turns -0.0 into +0.0 (IEEE addition; the compiler may not drop it), so the
+// two zeros are one key.  Every finite or infinite logit maps to a key of at
+// least 0x007fffff; 0 marks "no candidate".
+__device__ __forceinline__ uint32_t logit_key(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float key_logit(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Lane exchanges inside aligned groups of 8 lanes (DPP, no LDS round trip):
-// kXor1 / kXor2 swap neighbours / pairs within a quad, kMirror8 maps lane i of
-// a half row to lane 7 - i.  After kXor1 and kXor2 every lane of a quad holds
-// the quad's result, so kMirror8 then combines the two quads.
-constexpr int kXor1 = 0xb1;      // quad_perm [1, 0, 3, 2]
-constexpr int kXor2 = 0x4e;      // quad_perm [2, 3, 0, 1]
-constexpr int kMirror8 = 0x141;  // row_half_mirror
+// Lane exchanges inside aligned groups of P = 8 or 16 lanes (DPP, no LDS
+// round trip): kXor1 / kXor2 swap neighbours / pairs within a quad, kMirror8
+// maps lane i of a half row to lane 7 - i, kMirror16 lane i of a row to 15 - i.
+// After the steps for the smaller groups every lane of a group holds the
+// group's result, so each mirror step combines two such groups.
+constexpr int kXor1 = 0xb1;       // quad_perm [1, 0, 3, 2]
+constexpr int kXor2 = 0x4e;       // quad_perm [2, 3, 0, 1]
+constexpr int kMirror8 = 0x141;   // row_half_mirror
+constexpr int kMirror16 = 0x140;  // row_mirror
 
+// Every source lane of these patterns exists, so bound_ctrl (read 0 from a
+// missing lane) never applies; it lets the compiler fold the move into the
+// instruction that consumes it.
 template <int kCtrl>
 __device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, 0xf, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xf, 0xf, true);
 }
 
-// Max over the 8 lanes of (key, n) pairs ordered by key, then n (n = ~id:
-// the lower id wins a tie).  32-bit operations only.
-template <int kCtrl>
-__device__ __forceinline__ void pair_max_step(uint32_t& k, uint32_t& n) {
-  const uint32_t ok = dpp32<kCtrl>(k), on = dpp32<kCtrl>(n);
-  const bool take = ok > k || (ok == k && on > n);
-  k = take ? ok : k;
-  n = take ? on : n;
+// op over aligned groups of N lanes (N = 1, 2, 4, 8 or 16), result in all of them.
+template <int N, typename Op>
+__device__ __forceinline__ uint32_t lanes_reduce(uint32_t x, Op op) {
+  if constexpr (N >= 2) x = op(x, dpp32<kXor1>(x));
+  if constexpr (N >= 4) x = op(x, dpp32<kXor2>(x));
+  if constexpr (N >= 8) x = op(x, dpp32<kMirror8>(x));
+  if constexpr (N >= 16) x = op(x, dpp32<kMirror16>(x));
+  return x;
 }
 
-__device__ __forceinline__ void max8_pair(uint32_t& k, uint32_t& n) {
-  pair_max_step<kXor1>(k, n);
-  pair_max_step<kXor2>(k, n);
-  pair_max_step<kMirror8>(k, n);
+template <int N>
+__device__ __forceinline__ uint32_t lanes_max(uint32_t x) {
+  return lanes_reduce<N>(x, [](uint32_t u, uint32_t v) { return max(u, v); });
 }
 
-__device__ __forceinline__ uint32_t or8_u32(uint32_t x) {
-  x |= dpp32<kXor1>(x);
-  x |= dpp32<kXor2>(x);
-  return x | dpp32<kMirror8>(x);
+template <int N>
+__device__ __forceinline__ uint32_t lanes_or(uint32_t x) {
+  return lanes_reduce<N>(x, [](uint32_t u, uint32_t v) { return u | v; });
 }
 
-// The same value in all 8 lanes: ((a0 + a1) + (a2 + a3)) + ((a4 + a5) + (a6 + a7)),
-// up to the order of operands of each addition, which does not change a sum.
-__device__ __forceinline__ float sum8_f32(float x) {
-  x = x + __uint_as_float(dpp32<kXor1>(__float_as_uint(x)));
-  x = x + __uint_as_float(dpp32<kXor2>(__float_as_uint(x)));
-  return x + __uint_as_float(dpp32<kMirror8>(__float_as_uint(x)));
+// The same value in all N lanes: a fixed tree of pairwise sums, up to the
+// order of operands of each addition, which does not change a sum.
+template <int N>
+__device__ __forceinline__ float lanes_sum(float x) {
+  return __uint_as_float(lanes_reduce<N>(__float_as_uint(x), [](uint32_t u, uint32_t v) {
+    return __float_as_uint(__uint_as_float(u) + __uint_as_float(v));
+  }));
+}
+
+// Runtime group width (2, 4 or 8 lanes of the token's P) for group scores.
+template <int P>
+__device__ __forceinline__ uint32_t group_max(uint32_t x, int lpg) {
+  if (lpg >= 2) x = max(x, dpp32<kXor1>(x));
+  if (lpg >= 4) x = max(x, dpp32<kXor2>(x));
+  if (P >= 16 && lpg >= 8) x = max(x, dpp32<kMirror8>(x));
+  return x;
 }
 
 // A lane's list: its best candidates, keys descending (0 = empty), with their
@@ -140,7 +149,7 @@ template <int KL>
 __device__ __forceinline__ void list_fill(uint32_t (&lk)[KL], int (&li)[KL], const float* row, int V, bool vec4,
                                           int id0, bool live, bool refill, uint32_t fk, int fid) {
   auto offer = [&](uint32_t u, int v) {
-    uint32_t key = live ? logit_key(u) : 0u;
+    uint32_t key = live ? logit_key(__uint_as_float(u)) : 0u;
     const int id = id0 + v;
     if (refill) key = (key < fk || (key == fk && id > fid)) ? key : 0u;
     list_insert<KL>(lk, li, key, id);
@@ -174,16 +183,16 @@ __device__ __forceinline__ void list_fill(uint32_t (&lk)[KL], int (&li)[KL], con
   }
 }
 
-// Routes token t with the 8 lanes of its lane group: writes its ids and
-// weights; returns its rank bitmask (same in the 8 lanes; 0 for t >= T) and
-// the expert ids of the lane's slots j = q * 8 + p in `sel` (-1: none).
-template <int KS>
+// Routes token t with the P lanes of its lane group: writes its ids and
+// weights; returns its rank bitmask (same in the P lanes; 0 for t >= T) and
+// the expert ids of the lane's slots j = q * P + p in `sel` (-1: none).
+template <int P, int KS>
 __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int lane, int (&sel)[KS]) {
 #pragma clang fp contract(off)
   constexpr int KL = kRouterList;
   const LayoutArgs& L = a.lay;
-  const int p = lane & (kRouterLanes - 1);
-  const int gbase = lane & ~(kRouterLanes - 1);
+  const int p = lane & (P - 1);
+  const int gbase = lane & ~(P - 1);
   const bool live = t < L.T;
 
   // 1-2. the lane's best KL candidates (rows t >= T read row T - 1 and offer nothing)
@@ -199,14 +208,12 @@ __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int 
   list_fill<KL>(lk, li, row, a.V, a.vec4 != 0, id0, live, false, 0u, 0);
   bool exhausted = lk[0] == 0u;
 
-  // 3. group-limited gating: 8 / G consecutive lanes form one group, so the
+  // 3. group-limited gating: P / G consecutive lanes form one group, so the
   //    group score is the largest list head among them; lanes of groups that
   //    are not kept empty their lists.
   if (a.G > 1) {
-    const int lpg = kRouterLanes / a.G;
-    uint32_t m = lk[0];
-    if (lpg >= 2) m = max(m, dpp32<kXor1>(m));
-    if (lpg >= 4) m = max(m, dpp32<kXor2>(m));
+    const int lpg = P / a.G;
+    const uint32_t m = group_max<P>(lk[0], lpg);
     const int g = p / lpg;
     int better = 0;
     for (int q = 0; q < a.G; ++q) {
@@ -220,7 +227,9 @@ __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int 
     }
   }
 
-  // 4. k rounds over the 8 heads; slot j is kept by lane j % 8
+  // 4. k rounds over the P heads; slot j is kept by lane j % P.  Per round:
+  //    the largest head key, then the lowest id among the heads with that key
+  //    (two lane reductions); the owner pops its head (bitwise selects).
   uint32_t skey[KS];
 #pragma unroll
   for (int q = 0; q < KS; ++q) {
@@ -230,27 +239,26 @@ __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int 
   uint32_t key0 = 0u, fk = 0u;
   int fid = 0;
   for (int j = 0; j < L.k; ++j) {
-    uint32_t bk = lk[0], bn = ~(uint32_t)li[0];
-    max8_pair(bk, bn);
+    const uint32_t bk = lanes_max<P>(lk[0]);
+    const uint32_t bn = lanes_max<P>(lk[0] == bk ? ~(uint32_t)li[0] : 0u);
     const int id = (int)~bn;
     if (j == 0) key0 = bk;
 #pragma unroll
     for (int q = 0; q < KS; ++q) {  // no dynamic register indexing
-      if (j == q * kRouterLanes + p) {
-        sel[q] = id;
-        skey[q] = bk;
-      }
+      const bool mine_slot = j == q * P + p;
+      sel[q] = mine_slot ? id : sel[q];
+      skey[q] = mine_slot ? bk : skey[q];
     }
-    if (lk[0] == bk && li[0] == id) {  // the owner pops its head
-      fk = bk;
-      fid = id;
+    uint32_t own = lk[0] == bk && li[0] == id ? ~0u : 0u;  // the owner pops its head
+    __asm__("" : "+v"(own));
+    fk = bitsel(own, bk, fk);
+    fid = (int)bitsel(own, (uint32_t)id, (uint32_t)fid);
 #pragma unroll
-      for (int i = 0; i + 1 < KL; ++i) {
-        lk[i] = lk[i + 1];
-        li[i] = li[i + 1];
-      }
-      lk[KL - 1] = 0u;
+    for (int i = 0; i + 1 < KL; ++i) {
+      lk[i] = bitsel(own, lk[i + 1], lk[i]);
+      li[i] = (int)bitsel(own, (uint32_t)li[i + 1], (uint32_t)li[i]);
     }
+    lk[KL - 1] = bitsel(own, 0u, lk[KL - 1]);
     if (j >= KL - 1 && j + 1 < L.k) {  // a lane can run dry only after KL pops
       const bool need = !exhausted && lk[0] == 0u;
       if (__ballot(need)) {  // rare: a lane gave all KL of its entries
@@ -260,7 +268,7 @@ __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int 
     }
   }
 
-  // 5. weights, summed in a fixed order (per lane, then over the 8 lanes), and
+  // 5. weights, summed in a fixed order (per lane, then over the P lanes), and
   //    the rank bitmask
   float ev[KS];
   float sum = 0.0f;
@@ -278,13 +286,13 @@ __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int 
       rhi |= r >= 32 ? 1u << (r - 32) : 0u;
     }
   }
-  sum = sum8_f32(sum);
-  const uint64_t ranks = ((uint64_t)or8_u32(rhi) << 32) | or8_u32(rlo);
+  sum = lanes_sum<P>(sum);
+  const uint64_t ranks = ((uint64_t)lanes_or<P>(rhi) << 32) | lanes_or<P>(rlo);
 
   if (live) {
 #pragma unroll
     for (int q = 0; q < KS; ++q) {
-      const int j = q * kRouterLanes + p;
+      const int j = q * P + p;
       if (j < L.k) {
         a.topk_idx[(size_t)t * L.k + j] = sel[q];
         a.topk_w[(size_t)t * L.k + j] = ev[q] / sum;
@@ -297,24 +305,24 @@ __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int 
   return live ? ranks : 0;
 }
 
-// T > kFusedMaxTokens (so T >= 1): block b routes chunk b (64 tokens, 8 per wave) and
-// writes everything layout_count_kernel writes for it (rank bitmasks, mask
-// rows, chunk counts, an expert histogram row); layout_finalize_kernel (with
-// NB = number of chunks) completes the layout.
-template <int KS>
-__global__ __launch_bounds__(kRouterBlock) void router_count_kernel(RouterArgs a) {
+// T > kFusedMaxTokens (so T >= 1): block b routes chunk b (64 tokens, 64 / P
+// per wave) and writes everything layout_count_kernel writes for it (rank
+// bitmasks, mask rows, chunk counts, an expert histogram row);
+// layout_finalize_kernel (with NB = number of chunks) completes the layout.
+template <int P, int KS>
+__global__ __launch_bounds__(kWave * P) void router_count_kernel(RouterArgs a) {
   extern __shared__ int hist[];  // [E]
   __shared__ uint64_t chunk_masks[kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const LayoutArgs& L = a.lay;
-  for (int e = tid; e < L.E; e += kRouterBlock) hist[e] = 0;
+  for (int e = tid; e < L.E; e += kWave * P) hist[e] = 0;
   __syncthreads();
 
-  const int tw = wave * kRouterTokensPerWave + (lane >> 3);  // token within the chunk
+  const int tw = tid / P;  // token within the chunk
   const int t = blockIdx.x * kWave + tw;
-  const int p = lane & (kRouterLanes - 1);
+  const int p = lane & (P - 1);
   int sel[KS];
-  const uint64_t m = route_token<KS>(a, t, lane, sel);
+  const uint64_t m = route_token<P, KS>(a, t, lane, sel);
 #pragma unroll
   for (int q = 0; q < KS; ++q)
     if (sel[q] >= 0) atomicAdd(&hist[sel[q]], 1);
@@ -323,12 +331,12 @@ __global__ __launch_bounds__(kRouterBlock) void router_count_kernel(RouterArgs a
     uint8_t* dst = L.mask + (size_t)t * L.R;
     if (L.mask_words) {
       uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
-      for (int w = p; w < (L.R >> 2); w += kRouterLanes) {
+      for (int w = p; w < (L.R >> 2); w += P) {
         const uint32_t b = (uint32_t)(m >> (4 * w)) & 0xfu;
         d32[w] = (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
       }
     } else {
-      for (int r = p; r < L.R; r += kRouterLanes) dst[r] = (uint8_t)((m >> r) & 1u);
+      for (int r = p; r < L.R; r += P) dst[r] = (uint8_t)((m >> r) & 1u);
     }
   }
   if (p == 0) chunk_masks[tw] = m;
@@ -338,16 +346,16 @@ __global__ __launch_bounds__(kRouterBlock) void router_count_kernel(RouterArgs a
     const int cnt = wave_rank_counts(chunk_masks[lane], L.R, lane);
     if (lane < L.R) L.chunk_base[lane * L.NC + blockIdx.x] = cnt;
   }
-  for (int e = tid; e < L.E; e += kRouterBlock) L.block_expert[(size_t)blockIdx.x * L.E + e] = hist[e];
+  for (int e = tid; e < L.E; e += kWave * P) L.block_expert[(size_t)blockIdx.x * L.E + e] = hist[e];
 }
 
-// 1 <= T <= kFusedMaxTokens: one wave per 8 tokens, ids and weights only;
-// layout_fused_kernel follows on the ids.
-template <int KS>
+// 1 <= T <= kFusedMaxTokens: one wave per 64 / P tokens, ids and weights
+// only; layout_fused_kernel follows on the ids.
+template <int P, int KS>
 __global__ __launch_bounds__(kWave) void router_tokens_kernel(RouterArgs a) {
   const int lane = threadIdx.x;
   int sel[KS];
-  route_token<KS>(a, blockIdx.x * kRouterTokensPerWave + (lane >> 3), lane, sel);
+  route_token<P, KS>(a, blockIdx.x * (kWave / P) + lane / P, lane, sel);
 }
 
 }  // namespace moe

@@ -116,6 +116,8 @@ EDGES = [  # (label, T, E, k, R, gate, G, KG, ties, misalign)
     ("one group kept of 8", 500, 256, 8, 32, "softmax", 8, 1, True, False),
     ("R = 64", 1000, 256, 8, 64, "softmax", 8, 4, False, False),
     ("E = 1024", 300, 1024, 8, 16, "softmax", 8, 4, True, False),
+    ("8 lanes per token, two slots per lane", 150, 40, 12, 5, "softmax", 1, 1, True, False),
+    ("8 lanes per token, multi-block", 1500, 24, 5, 4, "sigmoid", 2, 1, True, False),
     ("E = 4096, multi-block", 1100, 4096, 16, 64, "sigmoid", 4, 2, False, False),
 ]
 
