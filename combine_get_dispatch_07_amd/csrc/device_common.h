@@ -24,12 +24,23 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int u = __shfl_up(v, d, kWave);
-    if (lane >= d) v += u;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP lane moves (no
+// LDS round trips): shifts by 1, 2, 4 and 8 within each row of 16 lanes
+// (lanes shifted in from outside a row read 0), then lane 15 of rows 0 and 2
+// is added to rows 1 and 3, then lane 31 to rows 2 and 3.  Every lane of the
+// wave must be active.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int dpp_or_zero(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xf, false);
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int /*lane*/) {
+  v += dpp_or_zero<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_or_zero<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_or_zero<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_or_zero<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_or_zero<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_or_zero<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 

@@ -17,7 +17,10 @@
 
 namespace moe {
 
-constexpr int kLayoutBlock = 256;      // tokens per block, multi-block path
+#ifndef MOE_LAYOUT_BLOCK
+#define MOE_LAYOUT_BLOCK 256
+#endif
+constexpr int kLayoutBlock = MOE_LAYOUT_BLOCK;  // tokens per block, multi-block path
 constexpr int kFusedMaxTokens = 1024;  // up to this many tokens one block does everything
 constexpr int kFusedMaxChunks = kFusedMaxTokens / kWave;
 
@@ -80,14 +83,22 @@ __device__ __forceinline__ void write_mask_row(const LayoutArgs& a, int t, uint6
   }
 }
 
-// Lane r (< R) returns how many lanes of the wave have bit r set in m.
-__device__ __forceinline__ int wave_rank_counts(uint64_t m, int R, int lane) {
-  int mine = 0;
-  for (int r = 0; r < R; ++r) {
-    const int c = __popcll(__ballot((m >> r) & 1ull));
-    mine = lane == r ? c : mine;
-  }
-  return mine;
+// Adds each lane's rank bits m to the per-rank counters cnt[0..63] (LDS)
+// with one atomic add per set bit: at most min(k, R) adds per lane, where one
+// ballot per rank would take R dependent steps.  Integer adds: the result
+// does not depend on their order.
+__device__ __forceinline__ void add_rank_bits(uint64_t m, int* cnt) {
+  for (uint64_t b = m; b; b &= b - 1) atomicAdd(&cnt[__builtin_ctzll(b)], 1);
+}
+
+// Lane r (< R) returns how many lanes of the wave have bit r set in m; `cnt`
+// is 64 ints of LDS private to the wave.
+__device__ __forceinline__ int wave_rank_counts(uint64_t m, int R, int lane, int* cnt) {
+  cnt[lane] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  add_rank_bits(m, cnt);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  return lane < R ? cnt[lane] : 0;
 }
 
 // Wave 0: per-rank totals -> tokens_per_rank and the exclusive rank offsets.
@@ -106,6 +117,7 @@ __device__ __forceinline__ void publish_rank_offsets(const LayoutArgs& a, const 
 __global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArgs a) {
   extern __shared__ int hist[];
   __shared__ int chunk_cnt[kWave * kFusedMaxChunks];
+  __shared__ int wave_cnt[kFusedMaxChunks][kWave];
   __shared__ int rank_total[kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   for (int e = tid; e < a.E; e += blockDim.x) hist[e] = 0;
@@ -116,7 +128,7 @@ __global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArg
     a.token_ranks[tid] = m;
     write_mask_row(a, tid, m);
   }
-  const int cnt = wave_rank_counts(m, a.R, lane);
+  const int cnt = wave_rank_counts(m, a.R, lane, wave_cnt[wave]);
   if (lane < a.R) chunk_cnt[lane * kFusedMaxChunks + wave] = cnt;
   __syncthreads();
 
@@ -136,6 +148,7 @@ __global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArg
 // Multi-block path, pass 1: mask rows, token bitmasks, chunk counts, block histograms.
 __global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a) {
   extern __shared__ int hist[];  // [E]
+  __shared__ int wave_cnt[kLayoutBlock / kWave][kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   for (int e = tid; e < a.E; e += kLayoutBlock) hist[e] = 0;
   __syncthreads();
@@ -147,7 +160,7 @@ __global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a
     write_mask_row(a, t, m);
   }
   const int chunk = t >> 6;
-  const int cnt = wave_rank_counts(m, a.R, lane);
+  const int cnt = wave_rank_counts(m, a.R, lane, wave_cnt[tid >> 6]);
   if (chunk < a.NC && lane < a.R) a.chunk_base[lane * a.NC + chunk] = cnt;
   __syncthreads();
   for (int e = tid; e < a.E; e += kLayoutBlock) a.block_expert[(size_t)blockIdx.x * a.E + e] = hist[e];
@@ -181,7 +194,7 @@ __global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutArgs a) {
       const int v = c < a.NC ? row[c] : 0;
       const int incl = wave_inclusive_scan(v, lane);
       if (c < a.NC) row[c] = carry + incl - v;
-      carry += __shfl(incl, kWave - 1, kWave);
+      carry += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
     if (lane == 0) rank_total[r] = carry;
   }

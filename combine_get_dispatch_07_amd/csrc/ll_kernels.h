@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void ll_scan_kernel(LlLayoutArgs a) {
     const int v = c < a.NC ? row[c] : 0;
     const int incl = wave_inclusive_scan(v, lane);
     if (c < a.NC) row[c] = carry + incl - v;
-    carry += __shfl(incl, kWave - 1, kWave);
+    carry += __builtin_amdgcn_readlane(incl, kWave - 1);
   }
   if (lane == 0) a.recv_count[e] = carry;
 }

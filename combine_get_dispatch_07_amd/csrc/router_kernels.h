@@ -312,10 +312,11 @@ __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int 
 template <int P, int KS>
 __global__ __launch_bounds__(kWave * P) void router_count_kernel(RouterArgs a) {
   extern __shared__ int hist[];  // [E]
-  __shared__ uint64_t chunk_masks[kWave];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  __shared__ int chunk_cnt[kWave];  // per-rank token counts of this chunk
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const LayoutArgs& L = a.lay;
   for (int e = tid; e < L.E; e += kWave * P) hist[e] = 0;
+  if (tid < kWave) chunk_cnt[tid] = 0;
   __syncthreads();
 
   const int tw = tid / P;  // token within the chunk
@@ -339,13 +340,10 @@ __global__ __launch_bounds__(kWave * P) void router_count_kernel(RouterArgs a) {
       for (int r = p; r < L.R; r += P) dst[r] = (uint8_t)((m >> r) & 1u);
     }
   }
-  if (p == 0) chunk_masks[tw] = m;
+  if (p == 0) add_rank_bits(m, chunk_cnt);
   __syncthreads();
 
-  if (wave == 0) {
-    const int cnt = wave_rank_counts(chunk_masks[lane], L.R, lane);
-    if (lane < L.R) L.chunk_base[lane * L.NC + blockIdx.x] = cnt;
-  }
+  if (tid < L.R) L.chunk_base[tid * L.NC + blockIdx.x] = chunk_cnt[tid];
   for (int e = tid; e < L.E; e += kWave * P) L.block_expert[(size_t)blockIdx.x * L.E + e] = hist[e];
 }
 
