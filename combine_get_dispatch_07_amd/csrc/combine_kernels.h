@@ -8,7 +8,7 @@
 // acc = fl32(acc + fl32(w_j * y[row(t, j)])); out = bf16_rne(acc).
 // row(t, j) is send_row[t, rank(e_j)] for the rank layout, or
 // e_j * cap + slot_pos[t, j] for the per-expert (low-latency) layout.  The
-// same gather with weight 1 over the token's distinct rank rows (j = rank,
+// same gather with weight 1 over the token's distinct rank rows (ranks
 // ascending) is the dispatch backward: grad_x[t] = sum_r grad_recv[send_row[t, r]].
 //
 // A gather, not a scatter: each (token, 512-channel slice) is owned by one
@@ -35,7 +35,7 @@ constexpr int kSlotBatch = 8;
 enum RowMode : int {
   kRankSlots = 0,    // j = slot: row send_row[t, rank(e_j)], weight topk_w[t, j]
   kExpertSlots = 1,  // j = slot: row e_j * cap + slot_pos[t, j], weight topk_w[t, j]
-  kRankRows = 2,     // j = rank: row send_row[t, j], weight 1
+  kRankRows = 2,     // j-th rank the token was sent to (ascending): row send_row[t, r_j], weight 1
 };
 
 struct CombineArgs {
@@ -49,7 +49,7 @@ struct CombineArgs {
   int T, H, H8, k, E, R;
   int cap;         // per-expert layout: rows per expert
   int num_y_rows;  // rows of y; slots whose row falls outside are skipped
-  int terms;       // terms per token: k, or R for kRankRows
+  int terms;       // terms per token: k, or min(k, R) for kRankRows
   int slices;
   int items;
 };
@@ -83,11 +83,21 @@ __device__ __forceinline__ RawMeta load_raw_meta(const CombineArgs& a, int item,
 // Lane j: the y row of term j, or -1.
 template <int kMode>
 __device__ __forceinline__ int resolve_row(const CombineArgs& a, const RawMeta& m, int item, int lane) {
+  if constexpr (kMode == kRankRows) {
+    // The token's rows on the ranks it was sent to, moved into lanes 0..n-1 in
+    // ascending rank order (so the sum order is unchanged); other lanes get -1.
+    // A token reaches at most min(k, R) ranks, so terms = min(k, R) lanes
+    // suffice however many ranks there are.
+    const bool valid = item < a.items && lane < a.R && (unsigned)m.rr < (unsigned)a.num_y_rows;
+    const uint64_t vm = __ballot(valid);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(vm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)vm, 0));
+    const int n = __popcll(vm);
+    const int dst = valid ? below : n + (lane - below);  // a permutation of the 64 lanes
+    return __builtin_amdgcn_ds_permute(dst << 2, valid ? m.rr : -1);
+  }
   bool valid = item < a.items && lane < a.terms;
   int row;
-  if constexpr (kMode == kRankRows) {
-    row = m.rr;
-  } else if constexpr (kMode == kExpertSlots) {
+  if constexpr (kMode == kExpertSlots) {
     valid = valid && (unsigned)m.id < (unsigned)a.E;
     row = valid && m.rr >= 0 && m.rr < a.cap ? m.id * a.cap + m.rr : -1;
   } else {

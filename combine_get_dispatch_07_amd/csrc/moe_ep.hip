@@ -114,7 +114,7 @@ void launch_dispatch(int U, dim3 grid, hipStream_t stream, const moe::DispatchAr
 
 // Waves per token in the combine backward (each takes every MOE_BWD_WAVES-th slice).
 #ifndef MOE_BWD_WAVES
-#define MOE_BWD_WAVES 4
+#define MOE_BWD_WAVES 7
 #endif
 static_assert(MOE_BWD_WAVES >= 1 && MOE_BWD_WAVES <= moe::kBwdMaxWaves, "waves per block");
 
@@ -182,7 +182,7 @@ moe_status launch_combine(moe::CombineArgs& a, void* out, hipStream_t stream) {
   const long resident = (long)stream_cu_count(stream) * MOE_COMBINE_WAVES_PER_CU / waves_per_block;
   const dim3 grid((unsigned)std::min<long>((a.items + waves_per_block - 1) / waves_per_block, resident));
   const dim3 block(moe::kCombineBlock);
-  a.terms = kMode == moe::kRankRows ? a.R : a.k;
+  a.terms = kMode == moe::kRankRows ? std::min(a.k, a.R) : a.k;
   if (a.terms <= moe::kSlotBatch)
     hipLaunchKernelGGL((moe::combine_pipelined_kernel<kMode>), grid, block, 0, stream, a);
   else

@@ -272,7 +272,9 @@ moe_status moe_combine_backward(const moe_shape* shape, const void* grad_out, co
  *   grad_recv_x       in  bf16[num_recv_rows, H]   gradient w.r.t. the received rows (FP8
  *                                                  dispatch is passed straight through)
  *   grad_recv_topk_w  in  float[num_recv_rows, k]  gradient w.r.t. recv_topk_w, or NULL
- *   topk_idx, send_row                             as given to / returned by moe_dispatch
+ *   topk_idx, send_row                             as given to / returned by moe_dispatch (a
+ *                                                  token has at most min(k, R) valid send_row
+ *                                                  entries; further ones are not read)
  *   grad_x            out bf16[T, H]    BF16_RNE(fp32 sum over ranks r ascending of
  *                                       grad_recv_x[send_row[t, r]]); +0 for unsent tokens
  *   grad_topk_w       out float[T, k]   grad_recv_topk_w[row(t, j), j], 0 for invalid slots;

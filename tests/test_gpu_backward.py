@@ -82,10 +82,13 @@ def test_backward_prefill_workload():
 @pytest.mark.parametrize("case", [
     # T, H, E, k, R, seed, invalid_frac
     (1, 256, 16, 4, 4, 1, 0.0),
-    (300, 512, 64, 6, 16, 2, 0.2),     # R > 8: dispatch backward takes the batched gather
+    (300, 512, 64, 6, 16, 2, 0.2),     # R > 8: rank rows compacted, min(k, R) = 6 terms
     (200, 256, 64, 12, 8, 3, 0.1),     # k > 8
     (129, 136, 32, 4, 8, 4, 0.0),      # ragged hidden
     (500, 256, 16, 4, 4, 5, 0.7),      # mostly invalid ids
+    (400, 256, 256, 8, 64, 6, 0.1),    # R = 64, the group-limited shape
+    (300, 256, 128, 16, 32, 7, 0.1),   # min(k, R) = 16: compacted rows in two batches
+    (100, 128, 64, 32, 64, 8, 0.0),    # k = 32: widest combine backward, four batches
 ])
 def test_backward_edges(case):
     run_backward_case(*case)
