@@ -504,6 +504,17 @@ def op_summary(bytes_: int, times_ms, kernel_us: float) -> dict:
     }
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown cpu"
+
+
 def cpu_baseline(cfg, W, budget_s: float = 20.0) -> dict:
     """The numpy oracle, as it stands, on the same workload (host cores)."""
     import numpy as np
@@ -535,8 +546,31 @@ def cpu_baseline(cfg, W, budget_s: float = 20.0) -> dict:
         "kind": "oracle",
         "sample": f"full {cfg.name} workload, layout+dispatch+combine, median of {len(times)} passes "
                   f"({med:.2f} s each); numpy elementwise work runs on one core "
-                  f"(host reports {os.cpu_count()} cpus)",
+                  f"(host: {_cpu_model()}, {os.cpu_count()} cpus, {len(os.sched_getaffinity(0))} in this "
+                  f"process's affinity)",
     }
+
+
+def copy_reference(torch, nbytes: int = 512 << 20, reps: int = 10) -> dict:
+    """A plain 512 MB device-to-device copy in the same run: the achievable-bandwidth reference
+    (read + write bytes over the copy time, median of `reps` event-timed copies)."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    us = sorted(times)[len(times) // 2]
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * nbytes, "us": round(us, 1), "GB_per_s": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3) -> None:
@@ -631,6 +665,9 @@ def main() -> int:
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload, dom),
                 "algorithmic_bytes_per_launch": ops[dom]["bytes"]}
 
+    log("timing a 512 MB device copy (achievable-bandwidth reference)")
+    copy_ref = copy_reference(torch)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -659,6 +696,7 @@ def main() -> int:
         "ops": ops,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "copy_reference": copy_ref,
     }
     if sec is not None:
         c2 = sec["cfg"]
