@@ -81,10 +81,19 @@ def bwd_algorithmic_bytes(cfg, n_recv: int) -> dict:
     }
 
 
-def kernel_source_hash() -> str:
+# The sources that decide what an op's kernels do: its kernel header, the shared device helpers
+# and the host code that picks launch shapes.
+OP_SOURCES = {
+    "dispatch": ("dispatch_kernels.h", "device_common.h", "moe_ep.hip"),
+    "combine": ("combine_kernels.h", "device_common.h", "moe_ep.hip"),
+    "layout": ("layout_kernels.h", "device_common.h", "moe_ep.hip"),
+}
+
+
+def kernel_source_hash(op: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_get_dispatch_07_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(OP_SOURCES[op]):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -97,7 +106,7 @@ def measured_traffic(workload: str, op: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(op):
         return None
     return rec.get("hbm_bytes_per_launch")
 

@@ -28,26 +28,29 @@ struct LlLayoutArgs {
 };
 
 // Builds this wave's expert masks for its 64 tokens and writes in-chunk slot
-// positions.  `mask` is this wave's [E] array in LDS, already zeroed.
+// positions.  `mask` is this wave's [E] array in LDS, already zeroed.  The
+// token's ids are loaded once (all loads issued together) and kept in
+// registers for both passes.
 __device__ __forceinline__ void ll_chunk_positions(const LlLayoutArgs& a, int chunk, int lane,
                                                    unsigned long long* mask) {
+  constexpr int kMaxK = 32;  // the library's top-k limit
   const int t = chunk * kWave + lane;
   const unsigned long long bit = 1ull << lane;
-  if (t < a.T) {
-    const int32_t* row = a.topk_idx + (size_t)t * a.k;
-    for (int j = 0; j < a.k; ++j) {
-      const int e = row[j];
-      if ((unsigned)e < (unsigned)a.E) atomicOr(&mask[e], bit);
-    }
-  }
+  const bool live = t < a.T;
+  const int32_t* row = a.topk_idx + (size_t)min(t, max(a.T - 1, 0)) * a.k;
+  int ids[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) ids[j] = live && j < a.k ? row[j] : -1;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if ((unsigned)ids[j] < (unsigned)a.E) atomicOr(&mask[ids[j]], bit);
   __syncthreads();
-  if (t < a.T) {
+  if (live) {
     const unsigned long long below = bit - 1ull;
-    const int32_t* row = a.topk_idx + (size_t)t * a.k;
-    for (int j = 0; j < a.k; ++j) {
-      const int e = row[j];
-      a.slot_local[(size_t)t * a.k + j] =
-          (unsigned)e < (unsigned)a.E ? __popcll(mask[e] & below) : -1;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < a.k)
+        a.slot_local[(size_t)t * a.k + j] = (unsigned)ids[j] < (unsigned)a.E ? __popcll(mask[ids[j]] & below) : -1;
     }
   }
 }
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(kDispatchBlock) void ll_dispatch_kernel(LlDispatchA
   }
   bool first = pos >= 0;
   for (int j = 0; j < a.k; ++j) {  // an earlier slot naming the same expert sends the row
-    const int other = __shfl(e, j, kWave);
+    const int other = __builtin_amdgcn_readlane(e, j);
     first = first && !(j < lane && other == e);
   }
 
