@@ -66,5 +66,25 @@ def build(out: Optional[str] = None, defines: Iterable[str] = (), extra_flags: I
     return out
 
 
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c_abi_client")
+
+
+def build_c_client(out: Optional[str] = None) -> str:
+    """Compile tests/c_abi_client.c, a plain C11 consumer of the C ABI (gcc, no HIP compiler),
+    linked against the in-tree libmoe_ep.so and the ROCm HIP runtime."""
+    out = out or C_CLIENT
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}",
+           f"-I{rocm}/include", C_CLIENT_SRC, "-o", out + ".tmp", f"-L{PKG_DIR}", "-lmoe_ep", f"-L{rocm}/lib",
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../combine_get_dispatch_07_amd", f"-Wl,-rpath,{rocm}/lib"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_client())
