@@ -8,11 +8,14 @@ the timed region.  Several independent buffer sets (identical inputs) are
 used in rotation, sized so that one set's data has left the 256 MB
 last-level cache before it is used again.
 
-Timed region: K steps of eager launches on the current stream, with HIP events
-between the ops (per-op times) and a barrier + synchronize on both sides
-(ms_per_step).  ``value`` = whole-step algorithmic bytes / step time.
-After it, each op is also timed as a HIP graph of back-to-back launches
-(``us_kernel``), which removes host launch gaps (they dominate at decode sizes).
+Timed region (``ms_per_step``, ``value``): K steps, each the replay of a HIP
+graph of layout -> dispatch -> combine captured on one buffer set (one graph
+per set, sets in rotation; every step runs all three kernels), bracketed by a
+synchronize on both sides.  ``value`` = whole-step algorithmic bytes / step
+time.  Graphs remove the host launch gaps that dominate at decode sizes; the
+same K steps as eager launches give ``ms_per_step_eager``, with HIP events
+between the ops for the per-op times (``us_mean``...).  Each op is also timed
+as a graph of back-to-back launches of that op alone (``us_kernel``).
 
     python bench.py [--steps K] [--warmup W] [--workload prefill|decode|...]
 
@@ -193,6 +196,33 @@ class Workload:
         wall = time.perf_counter() - t0
         per = {name: [e[i].elapsed_time(e[i + 1]) for e in ev] for i, name in enumerate(OPS)}
         return wall, per
+
+    def time_steps_graph(self, steps: int, warmup: int) -> float:
+        """Wall seconds for `steps` replays of per-set graphs of the whole step."""
+        torch = self.torch
+        stream = torch.cuda.Stream()
+        graphs = []
+        with torch.cuda.stream(stream):
+            for s in self.sets:
+                for name in OPS:  # warm-up on the capture stream
+                    self.op(name, s)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for name in OPS:
+                        self.op(name, s)
+                graphs.append(g)
+        n = len(graphs)
+        for i in range(warmup):
+            graphs[i % n].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[i % n].replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        del graphs
+        return wall
 
     def time_kernels(self, reps: int = 20, repeats: int = 5, ops=OPS) -> dict:
         """Per-op µs from HIP graphs of `reps` back-to-back launches over the rotating sets."""
@@ -632,10 +662,12 @@ def main() -> int:
         wl = Workload(cfg, torch, moe, W)
         log(f"timing {args.steps} steps of {name} (N_recv={wl.n_recv}, {len(wl.sets)} rotating sets "
             f"of {wl.footprint / 2**20:.0f} MiB)")
-        wall, per = wl.time_steps(args.steps, args.warmup)
+        wall_eager, per = wl.time_steps(args.steps, args.warmup)
+        wall = wl.time_steps_graph(args.steps, args.warmup)
         kern = {o: float("nan") for o in OPS} if args.no_kernel_timing else wl.time_kernels()
         ops = {o: op_summary(wl.bytes[o], per[o], kern[o]) for o in OPS}
         res = {"cfg": cfg, "n_recv": wl.n_recv, "ops": ops, "ms_per_step": wall * 1e3 / args.steps,
+               "ms_per_step_eager": wall_eager * 1e3 / args.steps,
                "step_bytes": sum(wl.bytes.values()), "sets": len(wl.sets)}
         if name == args.workload and args.cu_sweep:
             res["cu_budget"] = cu_sweep(wl, torch, moe)
@@ -691,6 +723,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(main_res["ms_per_step"], 4),
+        "ms_per_step_eager": round(main_res["ms_per_step_eager"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -712,6 +745,7 @@ def main() -> int:
         line["secondary"] = {"workload": f"{c2.name}: T={c2.num_tokens} H={c2.hidden} E={c2.num_experts} "
                                          f"top-{c2.num_topk} R={c2.num_ranks} {c2.dispatch_dtype} dispatch",
                              "n_recv": sec["n_recv"], "ms_per_step": round(sec["ms_per_step"], 4),
+                             "ms_per_step_eager": round(sec["ms_per_step_eager"], 4),
                              "ops": sec["ops"]}
         for key in ("low_latency", "router"):
             if key in sec:

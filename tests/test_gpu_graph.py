@@ -1,0 +1,98 @@
+"""The path captured in a HIP graph: layout (or the fused router) -> dispatch -> combine recorded
+once and replayed several times, with eager work and a poisoning of every output between the
+replays; each replay must reproduce the eager results bit for bit.  The library's kernels take
+all their sizes as arguments and clear nothing with memset, so a captured call is a faithful
+replay of the eager one."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+POISON = 0x5A
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _buffers(moe, shape, dtype, routed):
+    lay = moe.alloc_route(shape) if routed else moe.alloc_layout(shape)
+    d = moe.alloc_dispatch(shape, dtype)
+    out = torch.empty((shape.num_tokens, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    return lay, d, out
+
+
+def _step(moe, shape, dtype, x, idx, w, logits, y, lay, d, out, gate):
+    if logits is not None:
+        moe.run_route(shape, logits, lay, gate)
+        idx, w = lay["topk_idx"], lay["topk_w"]
+    else:
+        moe.run_layout(shape, idx, lay)
+    moe.run_dispatch(shape, dtype, x, idx, w, lay, d)
+    moe.moe_combine(shape, y, idx, w, d["send_row"], out)
+
+
+def _results(lay, d, out):
+    r = {k: v.clone() for k, v in d.items() if v is not None}
+    r["out"] = out.clone()
+    for k in ("tokens_per_rank", "tokens_per_expert", "is_token_in_rank", "topk_idx", "topk_w"):
+        if k in lay:
+            r[k] = lay[k].clone()
+    return r
+
+
+@pytest.mark.parametrize("name,T,routed", [("decode", 128, False), ("prefill", 2048, False), ("decode", 128, True),
+                                           ("prefill", 2048, True)])
+def test_graph_replays_match_eager(name, T, routed):
+    import combine_get_dispatch_07_amd as moe
+    from tests.gpu_harness import to_dev_bf16
+
+    cfg = W.with_tokens(W.CONFIG_BY_NAME[name], T)
+    print(f"[case] graph {name} T={T} routed={routed}", flush=True)
+    gate = "sigmoid" if cfg.routing == "sigmoid" else "softmax"
+    dtype = cfg.dispatch_dtype
+    shape = moe.MoeShape(cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks)
+    inp = W.make_inputs(cfg)
+    x = to_dev_bf16(inp["x"])
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    w = torch.from_numpy(inp["topk_w"]).cuda()
+    logits = torch.from_numpy(W.config_logits(cfg)).cuda() if routed else None
+    y = to_dev_bf16(W.draw_expert_outputs(np.random.default_rng(3), shape.num_tokens * min(shape.num_topk,
+                                                                                              shape.num_ranks),
+                                          shape.hidden))
+
+    lay, d, out = _buffers(moe, shape, dtype, routed)
+    _step(moe, shape, dtype, x, idx, w, logits, y, lay, d, out, gate)
+    torch.cuda.synchronize()
+    eager = _results(lay, d, out)
+
+    lay, d, out = _buffers(moe, shape, dtype, routed)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        _step(moe, shape, dtype, x, idx, w, logits, y, lay, d, out, gate)  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            _step(moe, shape, dtype, x, idx, w, logits, y, lay, d, out, gate)
+    bufs = [t for t in list(d.values()) + list(lay.values()) + [out] if t is not None]
+    for replay in range(3):
+        for t in bufs:  # every output must be rewritten by the replay
+            t.view(torch.uint8).fill_(POISON)
+        scratch = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        got = _results(lay, d, out)
+        n = int(eager["num_recv"].item())
+        assert int(got["num_recv"].item()) == n, f"replay {replay}"
+        for k, v in eager.items():
+            a, b = v, got[k]
+            if k in ("recv_x", "recv_scales", "recv_src_idx", "recv_topk_idx", "recv_topk_w"):
+                a, b = a[:n], b[:n]  # rows at or beyond num_recv are not written
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {replay}: {k}"
+    del g
