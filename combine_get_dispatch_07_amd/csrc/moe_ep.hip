@@ -626,9 +626,9 @@ moe_status moe_combine_backward(const moe_shape* shape, const void* grad_out, co
   const int slices = (a.H8 + moe::kWave - 1) / moe::kWave;
   const dim3 grid(s.num_tokens), block(std::min(slices, MOE_BWD_WAVES) * moe::kWave);
   if (s.num_topk <= 8)
-    hipLaunchKernelGGL(moe::combine_backward_kernel<8>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(moe::combine_backward_kernel, grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(moe::combine_backward_kernel<moe::kMaxTopk>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(moe::combine_backward_wide_kernel, grid, block, 0, stream, a);
   return last_launch_status();
 }
 

@@ -89,6 +89,7 @@ def test_backward_prefill_workload():
     (400, 256, 256, 8, 64, 6, 0.1),    # R = 64, the group-limited shape
     (300, 256, 128, 16, 32, 7, 0.1),   # min(k, R) = 16: compacted rows in two batches
     (100, 128, 64, 32, 64, 8, 0.0),    # k = 32: widest combine backward, four batches
+    (150, 136, 64, 32, 4, 9, 0.1),     # k = 32 on 4 ranks: eight slots share each y row, ragged hidden
 ])
 def test_backward_edges(case):
     run_backward_case(*case)
