@@ -68,11 +68,12 @@ __device__ __forceinline__ void bwd_reduce_dots(const CombineBwdArgs& a, const f
 #pragma clang fp contract(off)
 #pragma unroll
   for (int jj = 0; jj < N; ++jj) {
-    if (jj >= n) break;
-    float v = dot[jj];
+    if (jj < n) {
+      float v = dot[jj];
 #pragma unroll
-    for (int m = kWave / 2; m >= 1; m >>= 1) v = v + __shfl_xor(v, m, kWave);
-    if (lane == 0) partial[wave][jj] = v;
+      for (int m = kWave / 2; m >= 1; m >>= 1) v = v + __shfl_xor(v, m, kWave);
+      if (lane == 0) partial[wave][jj] = v;
+    }
   }
   __syncthreads();
   if (threadIdx.x < a.k) {  // wave 0, lane j: its own `valid` is slot j's

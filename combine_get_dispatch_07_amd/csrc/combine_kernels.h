@@ -27,6 +27,19 @@ namespace moe {
 #ifndef MOE_COMBINE_NT_STORE
 #define MOE_COMBINE_NT_STORE 1
 #endif
+// Expert-output rows are read once: nontemporal loads (measured faster).
+#ifndef MOE_COMBINE_NT_LOAD
+#define MOE_COMBINE_NT_LOAD 1
+#endif
+
+// One 16-byte piece of an expert-output row.
+__device__ __forceinline__ u32x4 load_y(const u32x4* p) {
+#if MOE_COMBINE_NT_LOAD
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
 
 constexpr int kCombineBlock = 256;
 constexpr int kSlotBatch = 8;
@@ -161,7 +174,7 @@ __device__ __forceinline__ void load_payload(const CombineArgs& a, const SlotRow
 #pragma unroll
   for (int j = 0; j < kSlotBatch; ++j) {
     const u32x4* yrow = reinterpret_cast<const u32x4*>(a.y + (size_t)max(r.row[j], 0) * a.H);
-    v[j] = yrow[c];
+    v[j] = load_y(yrow + c);
   }
 }
 
@@ -241,7 +254,7 @@ __global__ __launch_bounds__(kCombineBlock) void combine_persistent_kernel(Combi
       for (int jj = 0; jj < kSlotBatch; ++jj) {  // lanes >= terms hold row -1
         row[jj] = __builtin_amdgcn_readlane(slot_row, j0 + jj);
         w[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(slot_w), j0 + jj));
-        v[jj] = reinterpret_cast<const u32x4*>(a.y + (size_t)max(row[jj], 0) * a.H)[cc];
+        v[jj] = load_y(reinterpret_cast<const u32x4*>(a.y + (size_t)max(row[jj], 0) * a.H) + cc);
       }
 #pragma unroll
       for (int jj = 0; jj < kSlotBatch; ++jj)

@@ -118,10 +118,11 @@ void launch_dispatch(int U, dim3 grid, hipStream_t stream, const moe::DispatchAr
 #endif
 static_assert(MOE_BWD_WAVES >= 1 && MOE_BWD_WAVES <= moe::kBwdMaxWaves, "waves per block");
 
-// Resident combine waves per CU in the persistent launch (2 per SIMD, each
-// with two items' payload in flight).
+// Resident combine waves per CU in the persistent launch: one block of 4
+// waves, one per SIMD, each with two items' payload in flight.  Fewer
+// concurrent streams keep the rows being read at any time close together.
 #ifndef MOE_COMBINE_WAVES_PER_CU
-#define MOE_COMBINE_WAVES_PER_CU 8
+#define MOE_COMBINE_WAVES_PER_CU 4
 #endif
 
 // Compute units of the current device, queried once per device.
