@@ -19,7 +19,6 @@
 namespace moe {
 
 constexpr int kBwdMaxWaves = 16;  // upper bound of waves per block (one block per token)
-constexpr int kMaxTopk = 32;
 
 struct CombineBwdArgs {
   const uint16_t* g;  // [T, H] gradient of the combine output

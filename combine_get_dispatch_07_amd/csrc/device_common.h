@@ -7,6 +7,8 @@
 namespace moe {
 
 constexpr int kWave = 64;
+constexpr int kMaxTopk = 32;       // the library's limits (checked on the host)
+constexpr int kMaxExperts = 4096;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

@@ -78,44 +78,41 @@ __device__ __forceinline__ float block_amax(u32x4 v) {
   return __uint_as_float(m << 16);
 }
 
+// Every load is issued unconditionally from a clamped, always valid address
+// and masked afterwards: a load under a lane-dependent branch makes the
+// compiler wait for it before the branch joins, which would serialise the
+// loads (one memory round trip each) in this latency-bound kernel.
 template <int U, bool kFp8>
-__global__ __launch_bounds__(kDispatchBlock) void dispatch_kernel(DispatchArgs a) {
+__device__ __forceinline__ void dispatch_item(const DispatchArgs& a, int item, int lane) {
 #pragma clang fp contract(off)
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int item = blockIdx.x * (kDispatchBlock / kWave) + wave;
-
-  if (blockIdx.x == 0 && wave == 0) {  // publish the segment offsets and the row count
-    if (lane < a.R) a.rank_offsets[lane] = a.ws_rank_offsets[lane];
-    if (lane == 0) {
-      a.rank_offsets[a.R] = a.ws_rank_offsets[a.R];
-      *a.num_recv = a.ws_rank_offsets[a.R];
-    }
-  }
-  if (item >= a.items) return;
-
   const int t = item / a.slices;
   const int s = item - t * a.slices;
   const int chunk = t >> 6;
-  const int tl = t & (kWave - 1);
-
-  // Rank bitmasks of the chunk's 64 tokens, one per lane; this token's is uniform.
   const int tt = (chunk << 6) + lane;
-  const uint64_t lm = tt < a.T ? a.token_ranks[tt] : 0ull;
-  const uint64_t mine = readlane64(lm, tl) & a.rank_bits;
-  const uint64_t lanes_below = tl == 0 ? 0ull : (~0ull >> (kWave - tl));
-  // Lane r < R: first receive row of this chunk in rank r's segment.
-  const int chunk_row = lane < a.R ? a.ws_rank_offsets[lane] + a.chunk_base[lane * a.NC + chunk] : 0;
-
-  // Load this lane's U 16-byte pieces of the slice (8 bf16 channels each).
+  const int rl = min(lane, a.R - 1);
   const int c0 = s * (U * kWave) + lane;
   const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H);
+  const int jl = min(lane, a.k - 1);
+
+  // All loads first: the chunk's rank bitmasks (one per lane), lane r's segment
+  // offset and chunk base, slot metadata (lane j = slot j) and the x slice.
+  const uint64_t lm_raw = a.token_ranks[min(tt, a.T - 1)];
+  const int seg = a.ws_rank_offsets[rl];
+  const int cb = a.chunk_base[rl * a.NC + chunk];
+  const int ej_raw = a.topk_idx[(size_t)t * a.k + jl];
+  const float wj_raw = a.topk_w[(size_t)t * a.k + jl];
   u32x4 v[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c = c0 + u * kWave;
-    v[u] = c < a.H8 ? __builtin_nontemporal_load(xrow + c) : u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(xrow + min(c0 + u * kWave, a.H8 - 1));
+
+  const uint64_t lm = tt < a.T ? lm_raw : 0ull;
+  const uint64_t mine = readlane64(lm, t & (kWave - 1)) & a.rank_bits;
+  const int tl = t & (kWave - 1);
+  const uint64_t lanes_below = tl == 0 ? 0ull : (~0ull >> (kWave - tl));
+  const int chunk_row = lane < a.R ? seg + cb : 0;  // lane r < R: first receive row of this chunk on rank r
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (c0 + u * kWave >= a.H8) v[u] = u32x4{0u, 0u, 0u, 0u};
 
   u32x2 q[U];
   float sc[U];
@@ -130,13 +127,9 @@ __global__ __launch_bounds__(kDispatchBlock) void dispatch_kernel(DispatchArgs a
 
   // Slot metadata: lane j < k holds slot j of this token.
   const bool meta = s == 0;
-  int ej = -1, rj = -1;
-  float wj = 0.0f;
-  if (meta && lane < a.k) {
-    ej = a.topk_idx[(size_t)t * a.k + lane];
-    wj = a.topk_w[(size_t)t * a.k + lane];
-    if ((unsigned)ej < (unsigned)a.E) rj = rank_of(ej, a.rank_magic);
-  }
+  const int ej = lane < a.k ? ej_raw : -1;
+  const float wj = lane < a.k ? wj_raw : 0.0f;
+  const int rj = (unsigned)ej < (unsigned)a.E ? rank_of(ej, a.rank_magic) : -1;
 
   int my_row = -1;  // lane r: receive row of (t, r)
   uint64_t todo = mine;
@@ -178,6 +171,23 @@ __global__ __launch_bounds__(kDispatchBlock) void dispatch_kernel(DispatchArgs a
     }
   }
   if (meta && lane < a.R) a.send_row[(size_t)t * a.R + lane] = my_row;
+}
+
+template <int U, bool kFp8>
+__global__ __launch_bounds__(kDispatchBlock) void dispatch_kernel(DispatchArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x * (kDispatchBlock / kWave) + wave;
+  if (item < a.items) dispatch_item<U, kFp8>(a, item, lane);
+  if (blockIdx.x == 0 && wave == 0) {  // publish the segment offsets and the row count
+    const int off = a.ws_rank_offsets[lane < a.R ? lane : a.R];
+    if (lane < a.R) a.rank_offsets[lane] = off;
+    if (lane == 0) {
+      const int total = a.ws_rank_offsets[a.R];
+      a.rank_offsets[a.R] = total;
+      *a.num_recv = total;
+    }
+  }
 }
 
 }  // namespace moe

@@ -40,30 +40,37 @@ struct LayoutArgs {
 };
 
 // Rank bitmask of token t; valid expert ids are added to the LDS histogram.
+// The id loads are issued together, unconditionally, from clamped addresses
+// (a load under a lane-dependent branch or between LDS atomics would be
+// waited for on its own, one memory round trip each).  KI: ids held per lane
+// (k <= KI).
+template <int KI>
 __device__ __forceinline__ uint64_t token_rank_mask(const LayoutArgs& a, int t, int* hist) {
+  if (a.T == 0) return 0;  // no rows to read (topk_idx may be absent)
+  const int32_t* row = a.topk_idx + (size_t)min(t, a.T - 1) * a.k;
+  int ids[KI];
+  if (a.ids_vec4) {  // rows are 16-byte aligned: 4 ids per load
+    const int4* row4 = reinterpret_cast<const int4*>(row);
+#pragma unroll
+    for (int j = 0; j < KI / 4; ++j) {
+      const int4 q = row4[min(j, (a.k >> 2) - 1)];
+      ids[4 * j] = q.x;
+      ids[4 * j + 1] = q.y;
+      ids[4 * j + 2] = q.z;
+      ids[4 * j + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KI; ++j) ids[j] = row[min(j, a.k - 1)];
+  }
   uint64_t m = 0;
   if (t < a.T) {
-    const int32_t* row = a.topk_idx + (size_t)t * a.k;
-    if (a.ids_vec4) {  // rows are 16-byte aligned: 4 ids per load
-      const int4* row4 = reinterpret_cast<const int4*>(row);
-      for (int j = 0; j < (a.k >> 2); ++j) {
-        const int4 q = row4[j];
-        const int e4[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if ((unsigned)e4[i] < (unsigned)a.E) {
-            m |= 1ull << rank_of(e4[i], a.rank_magic);
-            atomicAdd(&hist[e4[i]], 1);
-          }
-        }
-      }
-    } else {
-      for (int j = 0; j < a.k; ++j) {
-        const int e = row[j];
-        if ((unsigned)e < (unsigned)a.E) {
-          m |= 1ull << rank_of(e, a.rank_magic);
-          atomicAdd(&hist[e], 1);
-        }
+    for (int j = 0; j < KI; ++j) {
+      const int e = ids[j];
+      if (j < a.k && (unsigned)e < (unsigned)a.E) {
+        m |= 1ull << rank_of(e, a.rank_magic);
+        atomicAdd(&hist[e], 1);
       }
     }
   }
@@ -114,6 +121,7 @@ __device__ __forceinline__ void publish_rank_offsets(const LayoutArgs& a, const 
 
 // T <= kFusedMaxTokens: one block of ceil(T/64) waves (at least one) does
 // everything in one launch.  Dynamic LDS: hist[E]; static: chunk counts [R][16].
+template <int KI>
 __global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArgs a) {
   extern __shared__ int hist[];
   __shared__ int chunk_cnt[kWave * kFusedMaxChunks];
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArg
   for (int e = tid; e < a.E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
 
-  const uint64_t m = token_rank_mask(a, tid, hist);
+  const uint64_t m = token_rank_mask<KI>(a, tid, hist);
   if (tid < a.T) {
     a.token_ranks[tid] = m;
     write_mask_row(a, tid, m);
@@ -146,6 +154,7 @@ __global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArg
 }
 
 // Multi-block path, pass 1: mask rows, token bitmasks, chunk counts, block histograms.
+template <int KI>
 __global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a) {
   extern __shared__ int hist[];  // [E]
   __shared__ int wave_cnt[kLayoutBlock / kWave][kWave];
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a
   __syncthreads();
 
   const int t = blockIdx.x * kLayoutBlock + tid;
-  const uint64_t m = token_rank_mask(a, t, hist);
+  const uint64_t m = token_rank_mask<KI>(a, t, hist);
   if (t < a.T) {
     a.token_ranks[t] = m;
     write_mask_row(a, t, m);

@@ -125,29 +125,30 @@ __global__ __launch_bounds__(kDispatchBlock) void ll_dispatch_kernel(LlDispatchA
   const int s = item - t * a.slices;
   const int chunk = t >> 6;
 
-  // lane j < k: slot j's expert, receive position, and whether it is the first slot naming it
-  int e = -1, pos = -1;
-  if (lane < a.k) {
-    e = a.topk_idx[(size_t)t * a.k + lane];
-    if ((unsigned)e < (unsigned)a.E) {
-      pos = a.chunk_base[(size_t)e * a.NC + chunk] + a.slot_local[(size_t)t * a.k + lane];
-      if ((unsigned)pos >= (unsigned)a.cap) pos = -1;  // only a plan from another layout gets here
-    }
-  }
+  // lane j < k: slot j's expert, receive position, and whether it is the first
+  // slot naming it.  Loads are unconditional from clamped addresses, so the x
+  // slice and the ids are in flight together (the chunk base needs the id).
+  const int jl = min(lane, a.k - 1);
+  const int e_raw = a.topk_idx[(size_t)t * a.k + jl];
+  const int local = a.slot_local[(size_t)t * a.k + jl];
+  const int c0 = s * (U * kWave) + lane;
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H);
+  u32x4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(xrow + min(c0 + u * kWave, a.H8 - 1));
+  const int e = lane < a.k ? e_raw : -1;
+  const bool valid = (unsigned)e < (unsigned)a.E;
+  const int base = a.chunk_base[(size_t)(valid ? e : 0) * a.NC + chunk];
+  int pos = valid ? base + local : -1;
+  if ((unsigned)pos >= (unsigned)a.cap) pos = -1;  // only a plan from another layout gets here
   bool first = pos >= 0;
   for (int j = 0; j < a.k; ++j) {  // an earlier slot naming the same expert sends the row
     const int other = __builtin_amdgcn_readlane(e, j);
     first = first && !(j < lane && other == e);
   }
-
-  const int c0 = s * (U * kWave) + lane;
-  const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H);
-  u32x4 v[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c = c0 + u * kWave;
-    v[u] = c < a.H8 ? __builtin_nontemporal_load(xrow + c) : u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int u = 0; u < U; ++u)
+    if (c0 + u * kWave >= a.H8) v[u] = u32x4{0u, 0u, 0u, 0u};
   u32x2 q[U];
   float sc[U];
   if constexpr (kFp8) {
@@ -184,6 +185,152 @@ __global__ __launch_bounds__(kDispatchBlock) void ll_dispatch_kernel(LlDispatchA
       for (int u = 0; u < U; ++u) {
         const int c = c0 + u * kWave;
         if (c < a.H8) __builtin_nontemporal_store(v[u], dst + c);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Small batches (T <= 1024): layout and dispatch in one launch.  Block t < T
+// owns token t.  Its waves take the hidden slices (one each) and, in 64-token
+// batches (one each), all T tokens' ids: a slot's position is the number of
+// earlier tokens naming its expert (ballot counts added into LDS), and the
+// token writes recv_count[e] = position + 1 for each expert no later token
+// names.  Block T writes recv_count[e] = 0 for the experts no token names.
+// All loads are issued together from clamped, always valid addresses and
+// masked afterwards (a load under a lane-dependent branch would be waited for
+// before the branch joins, one memory round trip per load).  Same rows,
+// positions and counts as the two-pass path.  KI: ids held per lane (k <= KI).
+constexpr int kLlSmallMaxTokens = 1024;
+constexpr int kLlSmallMaxWaves = 16;
+
+template <int U, bool kFp8, int KI>
+__global__ __launch_bounds__(kLlSmallMaxWaves * kWave) void ll_dispatch_small_kernel(LlDispatchArgs a,
+                                                                                      int32_t* recv_count) {
+#pragma clang fp contract(off)
+  __shared__ int cnt[kMaxTopk];    // slot j: earlier tokens naming its expert
+  __shared__ int after[kMaxTopk];  // slot j: later tokens naming its expert
+  __shared__ unsigned char named[kMaxExperts];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (a.T == 0) {  // no tokens (topk_idx may be absent): every count is 0
+    for (int e = threadIdx.x; e < a.E; e += blockDim.x) recv_count[e] = 0;
+    return;
+  }
+
+  // This wave's batch of tokens: lane l holds token 64 * wave + l's ids.
+  const int u = wave * kWave + lane;
+  const bool has_batch = wave * kWave < a.T;
+  int ids[KI];
+  {
+    const int32_t* row = a.topk_idx + (size_t)min(u, a.T - 1) * a.k;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) ids[i] = row[min(i, a.k - 1)];
+  }
+
+  if (blockIdx.x == a.T) {  // experts no token names
+    for (int e = threadIdx.x; e < a.E; e += blockDim.x) named[e] = 0;
+    __syncthreads();
+    if (u < a.T) {
+#pragma unroll
+      for (int i = 0; i < KI; ++i)
+        if (i < a.k && (unsigned)ids[i] < (unsigned)a.E) named[ids[i]] = 1;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < a.E; e += blockDim.x)
+      if (!named[e]) recv_count[e] = 0;
+    return;
+  }
+
+  const int t = blockIdx.x;
+  const int e_raw = a.topk_idx[(size_t)t * a.k + min(lane, a.k - 1)];
+  const int c0 = wave * (U * kWave) + lane;
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H);
+  u32x4 v[U];
+#pragma unroll
+  for (int uu = 0; uu < U; ++uu) v[uu] = __builtin_nontemporal_load(xrow + min(c0 + uu * kWave, a.H8 - 1));
+  if (threadIdx.x < kMaxTopk) {
+    cnt[threadIdx.x] = 0;
+    after[threadIdx.x] = 0;
+  }
+#pragma unroll
+  for (int i = 0; i < KI; ++i) ids[i] = i < a.k ? ids[i] : -1;
+  // lane j < k: slot j's expert, and whether it is the first slot naming it
+  const int e = lane < a.k ? e_raw : -1;
+  const bool valid = lane < a.k && (unsigned)e < (unsigned)a.E;
+  bool first = valid;
+  for (int j = 0; j < a.k; ++j) {
+    const int other = __builtin_amdgcn_readlane(e, j);
+    first = first && !(j < lane && other == e);
+  }
+  __syncthreads();
+
+  if (has_batch) {
+    const int d = t - wave * kWave;  // lanes l < d hold earlier tokens, l > d later ones
+    const uint64_t below = d <= 0 ? 0ull : d >= kWave ? ~0ull : (1ull << d) - 1ull;
+    const uint64_t above = d < 0 ? ~0ull : d >= kWave - 1 ? 0ull : ~((1ull << d << 1) - 1ull);
+    const uint64_t live = __ballot(u < a.T);
+    int n_before = 0, n_after = 0;  // lane j: slot j's counts over this batch
+    for (int j = 0; j < a.k; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      bool hit = false;
+#pragma unroll
+      for (int i = 0; i < KI; ++i) hit = hit || ids[i] == ej;
+      const uint64_t m = __ballot(hit) & live;
+      n_before = lane == j ? __popcll(m & below) : n_before;
+      n_after = lane == j ? __popcll(m & above) : n_after;
+    }
+    if (lane < a.k) {
+      if (n_before) atomicAdd(&cnt[lane], n_before);
+      if (n_after) atomicAdd(&after[lane], n_after);
+    }
+  }
+
+#pragma unroll
+  for (int uu = 0; uu < U; ++uu)
+    if (c0 + uu * kWave >= a.H8) v[uu] = u32x4{0u, 0u, 0u, 0u};
+  u32x2 q[U];
+  float sc[U];
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) {
+      sc[uu] = fmaxf(block_amax(v[uu]), kAmaxFloor) / kE4m3Max;
+      q[uu] = quantize8(v[uu], sc[uu]);
+    }
+  }
+  __syncthreads();
+
+  int pos = valid ? cnt[lane] : -1;
+  if (pos >= a.cap) pos = -1;  // unreachable: cap >= T is checked on the host
+  if (wave == 0) {
+    if (lane < a.k) a.slot_pos[(size_t)t * a.k + lane] = pos;
+    if (first && pos >= 0 && after[lane] == 0) recv_count[e] = pos + 1;  // the last token naming e
+  }
+  uint64_t todo = __ballot(first && pos >= 0);
+  while (todo) {
+    const int j = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    const int pj = __builtin_amdgcn_readlane(pos, j);
+    const size_t row = (size_t)ej * a.cap + pj;
+    if (wave == 0 && lane == 0) a.recv_src_idx[row] = t;
+    if constexpr (kFp8) {
+      u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.recv_x) + row * a.H);
+      float* sdst = a.recv_scales + row * (a.H / kFp8Block);
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const int c = c0 + uu * kWave;
+        if (c < a.H8) {
+          __builtin_nontemporal_store(q[uu], dst + c);
+          if ((lane & 15) == 0) sdst[c >> 4] = sc[uu];
+        }
+      }
+    } else {
+      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.recv_x) + row * a.H);
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const int c = c0 + uu * kWave;
+        if (c < a.H8) __builtin_nontemporal_store(v[uu], dst + c);
       }
     }
   }

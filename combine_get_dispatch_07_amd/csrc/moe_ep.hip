@@ -23,9 +23,9 @@
 
 namespace {
 
-constexpr int kMaxTopk = 32;
+constexpr int kMaxTopk = moe::kMaxTopk;
 constexpr int kMaxRanks = 64;
-constexpr int kMaxExperts = 4096;
+constexpr int kMaxExperts = moe::kMaxExperts;
 constexpr size_t kPlanAlign = 256;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxCuMaskWords = 32;  // up to 1024 compute units
@@ -121,6 +121,10 @@ static_assert(MOE_BWD_WAVES >= 1 && MOE_BWD_WAVES <= moe::kBwdMaxWaves, "waves p
 // Resident combine waves per CU in the persistent launch: one block of 4
 // waves, one per SIMD, each with two items' payload in flight.  Fewer
 // concurrent streams keep the rows being read at any time close together.
+// Small-batch low-latency dispatch in one launch (0: always the two-pass path).
+#ifndef MOE_LL_SMALL
+#define MOE_LL_SMALL 1
+#endif
 #ifndef MOE_COMBINE_WAVES_PER_CU
 #define MOE_COMBINE_WAVES_PER_CU 4
 #endif
@@ -208,6 +212,28 @@ LlPlanLayout ll_plan_layout(const moe_shape& s) {
   return p;
 }
 
+template <bool kFp8, int KI>
+void launch_ll_small_t(int U, dim3 grid, dim3 block, hipStream_t stream, const moe::LlDispatchArgs& a,
+                       int32_t* recv_count) {
+  if (U == 2)
+    hipLaunchKernelGGL((moe::ll_dispatch_small_kernel<2, kFp8, KI>), grid, block, 0, stream, a, recv_count);
+  else
+    hipLaunchKernelGGL((moe::ll_dispatch_small_kernel<1, kFp8, KI>), grid, block, 0, stream, a, recv_count);
+}
+
+void launch_ll_small(int U, bool fp8, dim3 grid, dim3 block, hipStream_t stream, const moe::LlDispatchArgs& a,
+                     int32_t* recv_count) {
+  const bool narrow = a.k <= 8;  // ids held per lane: 8, else the top-k limit
+  if (fp8 && narrow)
+    launch_ll_small_t<true, 8>(U, grid, block, stream, a, recv_count);
+  else if (fp8)
+    launch_ll_small_t<true, moe::kMaxTopk>(U, grid, block, stream, a, recv_count);
+  else if (narrow)
+    launch_ll_small_t<false, 8>(U, grid, block, stream, a, recv_count);
+  else
+    launch_ll_small_t<false, moe::kMaxTopk>(U, grid, block, stream, a, recv_count);
+}
+
 template <bool kFp8>
 void launch_ll_dispatch(int U, dim3 grid, hipStream_t stream, const moe::LlDispatchArgs& a) {
   const dim3 block(moe::kDispatchBlock);
@@ -230,7 +256,10 @@ void launch_router(int T, size_t lds, hipStream_t stream, const moe::RouterArgs&
       hipLaunchKernelGGL((moe::router_tokens_kernel<P, KS>), dim3(blocks), dim3(moe::kWave), 0, stream, a);
     }
     const int threads = std::max(moe::kWave, (T + moe::kWave - 1) / moe::kWave * moe::kWave);
-    hipLaunchKernelGGL(moe::layout_fused_kernel, dim3(1), dim3(threads), lds, stream, a.lay);
+    if (a.lay.k <= 8)
+      hipLaunchKernelGGL(moe::layout_fused_kernel<8>, dim3(1), dim3(threads), lds, stream, a.lay);
+    else
+      hipLaunchKernelGGL(moe::layout_fused_kernel<moe::kMaxTopk>, dim3(1), dim3(threads), lds, stream, a.lay);
   } else {
     hipLaunchKernelGGL((moe::router_count_kernel<P, KS>), dim3(a.lay.NC), dim3(moe::kWave * P), lds, stream, a);
     hipLaunchKernelGGL(moe::layout_finalize_kernel, dim3(1), dim3(1024), 0, stream, a.lay);
@@ -300,12 +329,19 @@ moe_status moe_get_dispatch_layout(const moe_shape* shape, const int32_t* topk_i
   a.ids_vec4 = (s.num_topk % 4 == 0 && aligned(topk_idx, 16)) ? 1 : 0;
   const size_t hist_bytes = (size_t)s.num_experts * sizeof(int);
 
+  const bool narrow = s.num_topk <= 8;  // ids held per lane: 8, else the top-k limit
   if (s.num_tokens <= moe::kFusedMaxTokens) {
     const int threads = std::max(moe::kWave, (s.num_tokens + moe::kWave - 1) / moe::kWave * moe::kWave);
-    hipLaunchKernelGGL(moe::layout_fused_kernel, dim3(1), dim3(threads), hist_bytes, stream, a);
+    if (narrow)
+      hipLaunchKernelGGL(moe::layout_fused_kernel<8>, dim3(1), dim3(threads), hist_bytes, stream, a);
+    else
+      hipLaunchKernelGGL(moe::layout_fused_kernel<moe::kMaxTopk>, dim3(1), dim3(threads), hist_bytes, stream, a);
   } else {
-    hipLaunchKernelGGL(moe::layout_count_kernel, dim3(p.NB), dim3(moe::kLayoutBlock), hist_bytes,
-                       stream, a);
+    if (narrow)
+      hipLaunchKernelGGL(moe::layout_count_kernel<8>, dim3(p.NB), dim3(moe::kLayoutBlock), hist_bytes, stream, a);
+    else
+      hipLaunchKernelGGL(moe::layout_count_kernel<moe::kMaxTopk>, dim3(p.NB), dim3(moe::kLayoutBlock), hist_bytes,
+                         stream, a);
     hipLaunchKernelGGL(moe::layout_finalize_kernel, dim3(1), dim3(1024), 0, stream, a);
   }
   return last_launch_status();
@@ -507,6 +543,34 @@ moe_status moe_dispatch_ll(const moe_shape* shape, moe_dtype dtype, const void* 
   const LlPlanLayout p = ll_plan_layout(s);
   if (workspace_bytes < p.total) return MOE_ERR_INVALID_ARG;
 
+  moe::LlDispatchArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.topk_idx = topk_idx;
+  a.recv_x = recv_x;
+  a.recv_scales = recv_scales;
+  a.recv_src_idx = recv_src_idx;
+  a.slot_pos = slot_pos;
+  a.T = s.num_tokens;
+  a.H = s.hidden;
+  a.H8 = s.hidden / 8;
+  a.k = s.num_topk;
+  a.E = s.num_experts;
+  a.NC = p.NC;
+  a.cap = expert_capacity;
+#if MOE_LL_SMALL
+  {  // small batch: one launch, one block per token (hidden up to 16384: 16 waves of 2 x 512 channels)
+    const int groups = (a.H8 + moe::kWave - 1) / moe::kWave;
+    const int U = groups <= moe::kLlSmallMaxWaves ? 1 : groups <= 2 * moe::kLlSmallMaxWaves ? 2 : 0;
+    if (s.num_tokens <= moe::kLlSmallMaxTokens && U > 0) {
+      const int waves = std::max({(groups + U - 1) / U, (s.num_tokens + moe::kWave - 1) / moe::kWave, 1});
+      a.slices = (groups + U - 1) / U;
+      a.items = s.num_tokens * a.slices;
+      launch_ll_small(U, fp8, dim3(s.num_tokens + 1), dim3(waves * moe::kWave), stream, a, recv_count);
+      return last_launch_status();
+    }
+  }
+#endif
+
   char* ws = static_cast<char*>(workspace);
   moe::LlLayoutArgs la{};
   la.topk_idx = topk_idx;
@@ -529,22 +593,8 @@ moe_status moe_dispatch_ll(const moe_shape* shape, moe_dtype dtype, const void* 
   st = last_launch_status();
   if (st != MOE_OK || s.num_tokens == 0) return st;
 
-  moe::LlDispatchArgs a{};
-  a.x = static_cast<const uint16_t*>(x);
-  a.topk_idx = topk_idx;
   a.slot_local = la.slot_local;
   a.chunk_base = la.chunk_base;
-  a.recv_x = recv_x;
-  a.recv_scales = recv_scales;
-  a.recv_src_idx = recv_src_idx;
-  a.slot_pos = slot_pos;
-  a.T = s.num_tokens;
-  a.H = s.hidden;
-  a.H8 = s.hidden / 8;
-  a.k = s.num_topk;
-  a.E = s.num_experts;
-  a.NC = p.NC;
-  a.cap = expert_capacity;
   const int U = pick_dispatch_chunks_per_lane(s.num_tokens, a.H8, fp8);
   const int groups = (a.H8 + moe::kWave - 1) / moe::kWave;
   a.slices = (groups + U - 1) / U;

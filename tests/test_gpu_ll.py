@@ -87,6 +87,8 @@ def test_ll_decode_workload():
     ("many_experts", 4, 200, 128, 4096, 32, "fp8", 0.1, 0),
     ("fused_wide", 5, 1024, 128, 512, 8, "fp8", 0.0, 0),
     ("ragged_hidden", 6, 300, 136, 32, 4, "bf16", 0.0, 3),
+    ("two_pass_wide_hidden", 7, 64, 16896, 16, 4, "bf16", 0.1, 0),  # hidden > 16384: two-pass path
+    ("small_last_batch", 8, 129, 256, 64, 8, "fp8", 0.0, 1),        # one token in the last 64-token batch
 ])
 def test_ll_edges(case):
     name, seed, T, H, E, k, dtype, inv, extra = case
