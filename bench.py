@@ -15,7 +15,8 @@ synchronize on both sides.  ``value`` = whole-step algorithmic bytes / step
 time.  Graphs remove the host launch gaps that dominate at decode sizes; the
 same K steps as eager launches give ``ms_per_step_eager``, with HIP events
 between the ops for the per-op times (``us_mean``...).  Each op is also timed
-as a graph of back-to-back launches of that op alone (``us_kernel``).
+as a graph of back-to-back launches of that op alone (``us_kernel``);
+``layout+dispatch`` is the send side end to end (both ops, same timings).
 
     python bench.py [--steps K] [--warmup W] [--workload prefill|decode|...]
 
@@ -136,7 +137,7 @@ class Workload:
         self.bytes = algorithmic_bytes(cfg, self.n_recv)
         footprint = sum(t.numel() * t.element_size() for t in self._tensors(first))
         if nsets is None:
-            nsets = max(2, min(16, -(-ROTATION_BYTES // footprint)))
+            nsets = max(3, min(16, -(-ROTATION_BYTES // footprint)))
         self.sets = [first]
         for _ in range(nsets - 1):
             s = self._new_set(x16, d)
@@ -169,6 +170,9 @@ class Workload:
         moe, cfg = self.moe, self.cfg
         if name == "layout":
             moe.run_layout(self.shape, s["idx"], s["lay"], stream)
+        elif name == "layout+dispatch":  # the end-to-end send side
+            self.op_on("layout", s, stream)
+            self.op_on("dispatch", s, stream)
         elif name == "dispatch":
             moe.run_dispatch(self.shape, cfg.dispatch_dtype, s["x"], s["idx"], s["w"], s["lay"], s["disp"], stream)
         else:
@@ -283,7 +287,7 @@ class LlWorkload(Workload):
         self.bytes = ll_algorithmic_bytes(cfg, self.n_recv)
         footprint = sum(t.numel() * t.element_size() for t in self._tensors(first))
         if nsets is None:
-            nsets = max(2, min(16, -(-ROTATION_BYTES // footprint)))
+            nsets = max(3, min(16, -(-ROTATION_BYTES // footprint)))
         self.sets = [first]
         for _ in range(nsets - 1):
             s_ = self._new_ll_set(x16, d)
@@ -612,6 +616,24 @@ def copy_reference(torch, nbytes: int = 512 << 20, reps: int = 10) -> dict:
     return {"bytes_moved": 2 * nbytes, "us": round(us, 1), "GB_per_s": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
 
 
+HBM_CEILING = os.path.join(ROOT, "combine_get_dispatch_07_amd", "hbm_ceiling")
+CEILING_MIX = {"dispatch": "read1_write5", "combine": "read5_write1"}  # the kernels' read/write mixes
+
+
+def hbm_ceiling():
+    """Best streaming bandwidth per read/write mix (csrc/hbm_ceiling.hip, built by build.py),
+    or None when the probe is not built."""
+    import subprocess
+
+    if not os.path.exists(HBM_CEILING):
+        log("hbm_ceiling is not built; skipping the streaming-bandwidth probe")
+        return None
+    res = subprocess.run([HBM_CEILING], capture_output=True, text=True, timeout=120)
+    if res.returncode != 0:
+        raise RuntimeError(f"hbm_ceiling failed ({res.returncode}): {res.stderr.strip()}")
+    return json.loads(res.stdout)
+
+
 def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3) -> None:
     """A plain device copy of known size, so counter runs can scale FETCH/WRITE_SIZE."""
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -633,6 +655,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the graph-replay per-op timing")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a 1 GiB device copy (counter runs)")
+    ap.add_argument("--no-hbm-ceiling", action="store_true", help="skip the streaming-bandwidth probe")
     ap.add_argument("--no-low-latency", action="store_true", help="skip the per-expert path on decode")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward ops on the main workload")
     ap.add_argument("--no-router", action="store_true", help="skip the fused router + layout timing")
@@ -664,8 +687,12 @@ def main() -> int:
             f"of {wl.footprint / 2**20:.0f} MiB)")
         wall_eager, per = wl.time_steps(args.steps, args.warmup)
         wall = wl.time_steps_graph(args.steps, args.warmup)
-        kern = {o: float("nan") for o in OPS} if args.no_kernel_timing else wl.time_kernels()
+        both = "layout+dispatch"
+        kern = ({o: float("nan") for o in OPS + (both,)} if args.no_kernel_timing
+                else wl.time_kernels(ops=OPS + (both,)))
+        per[both] = [a + b for a, b in zip(per["layout"], per["dispatch"])]  # event to event, both ops
         ops = {o: op_summary(wl.bytes[o], per[o], kern[o]) for o in OPS}
+        ops[both] = op_summary(wl.bytes["layout"] + wl.bytes["dispatch"], per[both], kern[both])
         res = {"cfg": cfg, "n_recv": wl.n_recv, "ops": ops, "ms_per_step": wall * 1e3 / args.steps,
                "ms_per_step_eager": wall_eager * 1e3 / args.steps,
                "step_bytes": sum(wl.bytes.values()), "sets": len(wl.sets)}
@@ -708,6 +735,14 @@ def main() -> int:
 
     log("timing a 512 MB device copy (achievable-bandwidth reference)")
     copy_ref = copy_reference(torch)
+    ceiling = None
+    if not args.no_hbm_ceiling:
+        log("measuring streaming bandwidth per read/write mix")
+        ceiling = hbm_ceiling()
+    if ceiling is not None:  # the same read/write mix as the dominant kernel, streamed without a gather
+        best = ceiling[CEILING_MIX[dom]]["GB_per_s"]
+        roofline["streaming_ceiling_same_mix"] = {"mix": CEILING_MIX[dom], "GB_per_s": best,
+                                                  "frac": round(achieved / best, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -739,6 +774,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "copy_reference": copy_ref,
+        "hbm_ceiling": ceiling,
     }
     if sec is not None:
         c2 = sec["cfg"]

@@ -85,6 +85,24 @@ def build_c_client(out: Optional[str] = None) -> str:
     return out
 
 
+HBM_CEILING_SRC = os.path.join(PKG_DIR, "csrc", "hbm_ceiling.hip")
+HBM_CEILING = os.path.join(PKG_DIR, "hbm_ceiling")
+
+
+def build_hbm_ceiling(out: Optional[str] = None) -> str:
+    """Compile csrc/hbm_ceiling.hip, the streaming-bandwidth probe bench.py reports beside the
+    kernels' fraction of peak (a standalone HIP program, not part of the library)."""
+    out = out or HBM_CEILING
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Wall",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", HBM_CEILING_SRC, "-o", out + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_c_client())
+    print(build_hbm_ceiling())
