@@ -56,7 +56,8 @@ __device__ __forceinline__ BwdSlots bwd_slots(const CombineBwdArgs& a, int t, in
   return m;
 }
 
-// Fixed-order reduction of the dot products: across lanes (xor tree), then
+// Fixed-order reduction of the dot products: across lanes (a DPP tree within
+// each row of 16 lanes, then rows 0 + 16 and 32 + 48, then those two), then
 // across the block's waves in ascending order.  dot[p] for p < n is reduced;
 // wave 0, lane j < k writes slot j's total, taken from dot[pos] (pos: lane j's
 // index into dot).
@@ -68,10 +69,12 @@ __device__ __forceinline__ void bwd_reduce_dots(const CombineBwdArgs& a, const f
 #pragma unroll
   for (int jj = 0; jj < N; ++jj) {
     if (jj < n) {
-      float v = dot[jj];
-#pragma unroll
-      for (int m = kWave / 2; m >= 1; m >>= 1) v = v + __shfl_xor(v, m, kWave);
-      if (lane == 0) partial[wave][jj] = v;
+      const int r = __float_as_int(lanes_sum<16>(dot[jj]));
+      const float lo = __int_as_float(__builtin_amdgcn_readlane(r, 0)) +
+                       __int_as_float(__builtin_amdgcn_readlane(r, 16));
+      const float hi = __int_as_float(__builtin_amdgcn_readlane(r, 32)) +
+                       __int_as_float(__builtin_amdgcn_readlane(r, 48));
+      if (lane == 0) partial[wave][jj] = lo + hi;
     }
   }
   __syncthreads();

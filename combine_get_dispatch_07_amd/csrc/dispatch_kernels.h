@@ -70,12 +70,9 @@ __device__ __forceinline__ float block_amax(u32x4 v) {
     m = max(m, v[i] & 0x7fffu);
     m = max(m, (v[i] >> 16) & 0x7fffu);
   }
-  // bf16 magnitudes order like their bit patterns, so the maximum is exact
-  m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 4, kWave));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 8, kWave));
-  return __uint_as_float(m << 16);
+  // bf16 magnitudes order like their bit patterns, so the maximum is exact;
+  // DPP lane moves within each row of 16 lanes (every lane must be active)
+  return __uint_as_float(lanes_max<16>(m) << 16);
 }
 
 // Every load is issued unconditionally from a clamped, always valid address

@@ -58,51 +58,9 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Lane exchanges inside aligned groups of P = 8 or 16 lanes (DPP, no LDS
-// round trip): kXor1 / kXor2 swap neighbours / pairs within a quad, kMirror8
-// maps lane i of a half row to lane 7 - i, kMirror16 lane i of a row to 15 - i.
-// After the steps for the smaller groups every lane of a group holds the
-// group's result, so each mirror step combines two such groups.
-constexpr int kXor1 = 0xb1;       // quad_perm [1, 0, 3, 2]
-constexpr int kXor2 = 0x4e;       // quad_perm [2, 3, 0, 1]
-constexpr int kMirror8 = 0x141;   // row_half_mirror
-constexpr int kMirror16 = 0x140;  // row_mirror
-
-// Every source lane of these patterns exists, so bound_ctrl (read 0 from a
-// missing lane) never applies; it lets the compiler fold the move into the
-// instruction that consumes it.
-template <int kCtrl>
-__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xf, 0xf, true);
-}
-
-// op over aligned groups of N lanes (N = 1, 2, 4, 8 or 16), result in all of them.
-template <int N, typename Op>
-__device__ __forceinline__ uint32_t lanes_reduce(uint32_t x, Op op) {
-  if constexpr (N >= 2) x = op(x, dpp32<kXor1>(x));
-  if constexpr (N >= 4) x = op(x, dpp32<kXor2>(x));
-  if constexpr (N >= 8) x = op(x, dpp32<kMirror8>(x));
-  if constexpr (N >= 16) x = op(x, dpp32<kMirror16>(x));
-  return x;
-}
-
-template <int N>
-__device__ __forceinline__ uint32_t lanes_max(uint32_t x) {
-  return lanes_reduce<N>(x, [](uint32_t u, uint32_t v) { return max(u, v); });
-}
-
 template <int N>
 __device__ __forceinline__ uint32_t lanes_or(uint32_t x) {
   return lanes_reduce<N>(x, [](uint32_t u, uint32_t v) { return u | v; });
-}
-
-// The same value in all N lanes: a fixed tree of pairwise sums, up to the
-// order of operands of each addition, which does not change a sum.
-template <int N>
-__device__ __forceinline__ float lanes_sum(float x) {
-  return __uint_as_float(lanes_reduce<N>(__float_as_uint(x), [](uint32_t u, uint32_t v) {
-    return __float_as_uint(__uint_as_float(u) + __uint_as_float(v));
-  }));
 }
 
 // Runtime group width (2, 4 or 8 lanes of the token's P) for group scores.
