@@ -15,6 +15,7 @@ import torch
 
 from ._lib import (LIB_PATH, MoeError, MoeShape, ll_workspace_bytes, max_recv_rows, moe_combine,  # noqa: F401
                    moe_combine_backward, moe_combine_ll, moe_dispatch, moe_dispatch_backward, moe_dispatch_ll,
+                   moe_encode_e4m3,
                    moe_get_dispatch_layout, moe_route_layout, status_string, stream_create_cu_range, stream_destroy,
                    workspace_bytes)
 

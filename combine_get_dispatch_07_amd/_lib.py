@@ -86,6 +86,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_dispatch_ll.restype = ctypes.c_int
     lib.moe_combine_ll.argtypes = [SH, P, I32, P, P, P, P, P]
     lib.moe_combine_ll.restype = ctypes.c_int
+    lib.moe_encode_e4m3.argtypes = [P, P, ctypes.c_int64, P]
+    lib.moe_encode_e4m3.restype = ctypes.c_int
     lib.moe_combine_backward.argtypes = [SH, P, P, I32, P, P, P, P, P, P]
     lib.moe_combine_backward.restype = ctypes.c_int
     lib.moe_dispatch_backward.argtypes = [SH, P, I32, P, P, P, P, P, P]
@@ -223,6 +225,17 @@ def moe_combine_ll(shape: MoeShape, y, topk_idx, topk_w, slot_pos, out, stream=N
         _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
         _ptr(slot_pos, "slot_pos", torch.int32, T * k), _ptr(out, "out", torch.bfloat16, T * H), _stream(stream))
     _check("moe_combine_ll", code)
+
+
+def moe_encode_e4m3(values, codes, stream=None) -> None:
+    """codes (uint8) = E4M3 round-to-nearest-even codes of values (float32), as the FP8 dispatch
+    rounds x / s; defined for finite |values| < 464."""
+    n = values.numel()
+    if codes.numel() != n:
+        raise ValueError(f"codes: {codes.numel()} elements for {n} values")
+    code = lib.moe_encode_e4m3(_ptr(values, "values", torch.float32, n), _ptr(codes, "codes", torch.uint8, n), n,
+                               _stream(stream))
+    _check("moe_encode_e4m3", code)
 
 
 def moe_combine_backward(shape: MoeShape, grad_out, y, topk_idx, topk_w, send_row, grad_y, grad_topk_w,

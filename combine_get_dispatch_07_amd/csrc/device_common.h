@@ -98,22 +98,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// fp32 -> OCP E4M3 ("fn": bias 7, max 448, no infinities) code, round to nearest
-// even, sign kept.  Magnitudes from 464 up saturate to 448 (RNE already maps
-// [448, 464] to 448), which the per-block scaling never exceeds.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  // normal range: keep 3 mantissa bits, round the other 20 to nearest even,
-  // then move the exponent bias from 127 to 7 (a carry rolls into the exponent)
-  const uint32_t rounded = a + 0x7ffffu + ((a >> 20) & 1u);
-  const uint32_t normal = (rounded >> 20) - (120u << 3);
-  // below 2^-6: multiples of 2^-9; a * 512 is exact and rint rounds ties to even
-  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  uint32_t code = a < 0x3c800000u ? sub : normal;
-  code = a >= 0x43e80000u ? 0x7eu : code;
-  return sign | code;
+// fp32 -> OCP E4M3 ("fn": bias 7, max 448, no infinities) codes of two values,
+// round to nearest even, sign kept (-0 and negative values that round to zero
+// give 0x80), with gfx950's v_cvt_pk_fp8_f32: the codes land in bytes 0-1
+// (kHi false) or 2-3 (kHi true) of `old`, whose other half is kept.  Checked
+// against round-to-nearest-even over every fp32 magnitude below 464, the range
+// the per-block scaling produces (|x / s| <= 448 (1 + 2^-23)^2); larger or
+// non-finite inputs are outside that contract.
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, kHi);
 }
 
 }  // namespace moe

@@ -47,19 +47,34 @@ struct DispatchArgs {
   int items;   // T * slices
 };
 
-// Eight bf16 channels of one lane -> eight E4M3 codes, given the block scale.
+// Eight bf16 channels of one lane -> eight E4M3 codes, given the block scale:
+// q = E4M3_RNE(fl32(x / s)), IEEE division, then the hardware conversion.
 __device__ __forceinline__ u32x2 quantize8(u32x4 v, float s) {
 #pragma clang fp contract(off)
-  uint32_t q[8];
+  float f[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    q[2 * i] = e4m3_rne(bf16_lo(v[i]) / s);
-    q[2 * i + 1] = e4m3_rne(bf16_hi(v[i]) / s);
+    f[2 * i] = bf16_lo(v[i]) / s;
+    f[2 * i + 1] = bf16_hi(v[i]) / s;
   }
   u32x2 out;
-  out[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-  out[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+#pragma unroll
+  for (int w = 0; w < 2; ++w)
+    out[w] = e4m3_pack2<true>(f[4 * w + 2], f[4 * w + 3], e4m3_pack2<false>(f[4 * w], f[4 * w + 1], 0u));
   return out;
+}
+
+// Standalone E4M3 encoding (moe_encode_e4m3): four values per thread.
+__global__ __launch_bounds__(256) void encode_e4m3_kernel(const float* in, uint8_t* out, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = i + j < n ? in[i + j] : 0.0f;
+  const uint32_t q = e4m3_pack2<true>(v[2], v[3], e4m3_pack2<false>(v[0], v[1], 0u));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (i + j < n) out[i + j] = (uint8_t)(q >> (8 * j));
 }
 
 // |x| maximum over the 16 lanes (128 channels) sharing a scale, as fp32.

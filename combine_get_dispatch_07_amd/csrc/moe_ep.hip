@@ -609,6 +609,15 @@ moe_status moe_dispatch_ll(const moe_shape* shape, moe_dtype dtype, const void* 
   return last_launch_status();
 }
 
+moe_status moe_encode_e4m3(const float* values, uint8_t* codes, int64_t n, hipStream_t stream) {
+  if (n < 0 || ((!values || !codes) && n > 0)) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  const int64_t blocks = (n + 1023) / 1024;  // 256 threads of 4 values
+  if (blocks > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(moe::encode_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, values, codes, n);
+  return last_launch_status();
+}
+
 moe_status moe_combine_ll(const moe_shape* shape, const void* y, int32_t expert_capacity, const int32_t* topk_idx,
                           const float* topk_w, const int32_t* slot_pos, void* out, hipStream_t stream) {
   moe_status st = check_shape(shape);

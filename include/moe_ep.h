@@ -182,6 +182,22 @@ moe_status moe_dispatch(const moe_shape* shape, moe_dtype dtype, const void* x,
                         float* recv_topk_w, int32_t* rank_offsets, int32_t* send_row,
                         int32_t* num_recv, hipStream_t stream);
 
+/* The E4M3 rounding the FP8 dispatch applies to x / s, on its own.
+ * [overlap notes, 节点内通信: FP8 transport.]
+ *
+ * codes[i] = the nearest OCP E4M3 ("fn": bias 7, max 448) value to values[i],
+ * ties to the even code, sign kept (negative values that round to zero give
+ * 0x80).  Defined for finite |values[i]| < 464, the range the dispatch's
+ * per-128-channel scaling produces; other inputs give unspecified codes.
+ *
+ *   values  in  float[n]   device memory
+ *   codes   out uint8[n]   device memory
+ *   n           number of values; 0 launches nothing
+ *
+ * MOE_ERR_INVALID_ARG for n < 0 or a NULL array with n > 0.
+ */
+moe_status moe_encode_e4m3(const float* values, uint8_t* codes, int64_t n, hipStream_t stream);
+
 /* Combine.  [overlap notes, 节点内通信: combine; rocSHMEM notes 3.2: the
  * receive buffer is reused for the returning expert outputs.]
  *

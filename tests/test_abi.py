@@ -163,3 +163,11 @@ def route(s, gate=0, G=1, KG=1, router=True, logits=A, idx=A, w=A, tpr=A, tpe=A,
 ])
 def test_route_layout_rejects(kw, shape_kw, code):
     assert route(shape(**shape_kw), **kw) == code
+
+
+def test_encode_e4m3_rejections():
+    enc = L.lib.moe_encode_e4m3
+    assert enc(A, A, -1, None) == INVALID
+    assert enc(None, A, 4, None) == INVALID
+    assert enc(A, None, 4, None) == INVALID
+    assert enc(None, None, 0, None) == OK  # nothing to launch
