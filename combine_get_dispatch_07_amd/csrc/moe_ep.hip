@@ -128,6 +128,9 @@ static_assert(MOE_BWD_WAVES >= 1 && MOE_BWD_WAVES <= moe::kBwdMaxWaves, "waves p
 #ifndef MOE_COMBINE_WAVES_PER_CU
 #define MOE_COMBINE_WAVES_PER_CU 4
 #endif
+#ifndef MOE_COMBINE_MAX_WAVES_PER_CU
+#define MOE_COMBINE_MAX_WAVES_PER_CU 16
+#endif
 
 // Compute units of the current device, queried once per device.
 int device_cu_count() {
@@ -184,7 +187,14 @@ moe_status launch_combine(moe::CombineArgs& a, void* out, hipStream_t stream) {
   if ((int64_t)a.T * a.slices > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   a.items = a.T * a.slices;
   const int waves_per_block = moe::kCombineBlock / moe::kWave;
-  const long resident = (long)stream_cu_count(stream) * MOE_COMBINE_WAVES_PER_CU / waves_per_block;
+  // A stream limited to fewer CUs keeps about the full chip's number of waves in
+  // flight (each CU then serves a larger share of the bandwidth), up to
+  // MOE_COMBINE_MAX_WAVES_PER_CU.
+  const long cus = stream_cu_count(stream);
+  const long per_cu = std::min<long>(MOE_COMBINE_MAX_WAVES_PER_CU,
+                                     std::max<long>(MOE_COMBINE_WAVES_PER_CU,
+                                                    (long)MOE_COMBINE_WAVES_PER_CU * device_cu_count() / cus));
+  const long resident = cus * per_cu / waves_per_block;
   const dim3 grid((unsigned)std::min<long>((a.items + waves_per_block - 1) / waves_per_block, resident));
   const dim3 block(moe::kCombineBlock);
   a.terms = kMode == moe::kRankRows ? std::min(a.k, a.R) : a.k;
