@@ -8,7 +8,7 @@ the timed region.  Several independent buffer sets (identical inputs) are
 used in rotation, sized so that one set's data has left the 256 MB
 last-level cache before it is used again.
 
-Timed region (``ms_per_step``, ``value``): K steps, each the replay of a HIP
+Timed region (``ms_per_step``, ``value``): K steps (default 200, after 100 warm-up steps), each the replay of a HIP
 graph of layout -> dispatch -> combine captured on one buffer set (one graph
 per set, sets in rotation; every step runs all three kernels), bracketed by a
 synchronize on both sides.  ``value`` = whole-step algorithmic bytes / step
@@ -648,8 +648,8 @@ def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--secondary", default="decode", help="second workload measured in the same run ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
