@@ -152,6 +152,9 @@ EDGE = [
     ("ragged_slice_bf16", 10, 200, 136, 32, 4, 8, "bf16", 0.0),
     ("R_not_multiple_of_4", 11, 333, 256, 30, 5, 6, "bf16", 0.1),
     ("R_64_k_8", 12, 2000, 256, 256, 8, 64, "bf16", 0.0),
+    ("wide_hidden_fp8", 13, 300, 16384, 64, 8, 8, "fp8", 0.0),     # 2048 16-byte pieces per row
+    ("wide_hidden_bf16", 14, 300, 16384, 64, 8, 8, "bf16", 0.05),
+    ("many_chunks", 15, 70000, 64, 64, 4, 8, "bf16", 0.05),      # 1094 chunks: multi-pass chunk scans
 ]
 
 
