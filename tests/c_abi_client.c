@@ -1,12 +1,15 @@
 /*
  * A plain C client of libmoe_ep.so: no torch, no C++, only the header and the HIP runtime.
  *
- * It builds a small batch with known routing, runs layout -> dispatch (bf16) -> combine through
- * the C ABI on device memory it allocates itself, and checks results it can predict exactly:
+ * It builds a small batch with known routing, runs layout -> dispatch (bf16) -> combine, the
+ * dispatch backward, the low-latency dispatch and combine, and the E4M3 encoder through the C ABI on
+ * device memory it allocates itself, and checks results it can predict exactly:
  *   - token t names experts (t % E) and ((t + 1) % E), weights 1.0 and 0.0, k = 2, R = 4, E = 8;
  *   - combining the received rows back (y = recv_x) must return x bit for bit, because the
- *     weight-1 slot contributes x exactly and the weight-0 slot adds +0;
- *   - the per-rank token counts follow from the routing by hand.
+ *     weight-1 slot contributes x exactly and the weight-0 slot adds +0 (both layouts);
+ *   - the per-rank and per-expert counts follow from the routing by hand;
+ *   - the dispatch backward of the received rows is x times the number of distinct ranks;
+ *   - E4M3 codes of exactly representable values, ties and signed zero are known.
  * Exit status 0 on success; prints what failed otherwise.
  */
 #include <stdint.h>
@@ -121,11 +124,84 @@ int main(void) {
     fprintf(stderr, "combine of the received rows did not return x\n");
     ++fails;
   }
+
+  /* dispatch backward of the received rows: each token gets x once per distinct rank it went to,
+   * i.e. x or 2x (exact: x is in [1, 2), so 2x adds one to the bf16 exponent field) */
+  uint16_t* dgx;
+  CHECK_HIP(hipMalloc((void**)&dgx, sizeof(x)));
+  CHECK_MOE(moe_dispatch_backward(&shape, drecv, n, NULL, didx, dsend, dgx, NULL, stream));
+  static uint16_t gx[T * H];
+  CHECK_HIP(hipMemcpyAsync(gx, dgx, sizeof(gx), hipMemcpyDeviceToHost, stream));
+  CHECK_HIP(hipStreamSynchronize(stream));
+  for (int t = 0; t < T && fails < 8; ++t) {
+    const int two = (t % E) / L != ((t + 1) % E) / L;
+    for (int c = 0; c < H; ++c) {
+      const uint16_t want = (uint16_t)(x[t * H + c] + (two ? 0x80 : 0));
+      if (gx[t * H + c] != want) {
+        fprintf(stderr, "dispatch backward: token %d channel %d = 0x%04x, want 0x%04x\n", t, c, gx[t * H + c], want);
+        ++fails;
+        break;
+      }
+    }
+  }
+
+  /* low-latency layout: per-expert buffers [E, T, H]; combining them back with weights 1 and 0
+   * returns x bit for bit */
+  const size_t ll_ws = moe_ll_workspace_bytes(&shape);
+  void* dllws;
+  uint16_t *dllx, *dllout;
+  int32_t *dllsrc, *dllcnt, *dllpos;
+  CHECK_HIP(hipMalloc(&dllws, ll_ws));
+  CHECK_HIP(hipMalloc((void**)&dllx, (size_t)E * T * H * sizeof(uint16_t)));
+  CHECK_HIP(hipMalloc((void**)&dllsrc, (size_t)E * T * sizeof(int32_t)));
+  CHECK_HIP(hipMalloc((void**)&dllcnt, E * sizeof(int32_t)));
+  CHECK_HIP(hipMalloc((void**)&dllpos, sizeof(idx)));
+  CHECK_HIP(hipMalloc((void**)&dllout, sizeof(x)));
+  CHECK_MOE(moe_dispatch_ll(&shape, MOE_BF16, dx, didx, dllws, ll_ws, T, dllx, NULL, dllsrc, dllcnt, dllpos, stream));
+  CHECK_MOE(moe_combine_ll(&shape, dllx, T, didx, dw, dllpos, dllout, stream));
+  int32_t cnt[E];
+  CHECK_HIP(hipMemcpyAsync(out, dllout, sizeof(out), hipMemcpyDeviceToHost, stream));
+  CHECK_HIP(hipMemcpyAsync(cnt, dllcnt, sizeof(cnt), hipMemcpyDeviceToHost, stream));
+  CHECK_HIP(hipStreamSynchronize(stream));
+  for (int e = 0; e < E; ++e) {
+    int want = 0; /* tokens naming e: t % E == e or (t + 1) % E == e */
+    for (int t = 0; t < T; ++t) want += (t % E == e) || ((t + 1) % E == e);
+    if (cnt[e] != want) {
+      fprintf(stderr, "recv_count[%d] = %d, want %d\n", e, cnt[e], want);
+      ++fails;
+    }
+  }
+  if (memcmp(out, x, sizeof(x)) != 0) {
+    fprintf(stderr, "low-latency combine of the received rows did not return x\n");
+    ++fails;
+  }
+
+  /* the E4M3 rounding on its own: exact values, ties to even, signed zero, the largest code */
+  const float fv[10] = {0.0f, -0.0f, 1.0f, -2.0f, 448.0f, 0x1p-9f, 0x1p-10f, 0x3p-10f, 1.0625f, 1.1875f};
+  const uint8_t fwant[10] = {0x00, 0x80, 0x38, 0xC0, 0x7E, 0x01, 0x00, 0x02, 0x38, 0x3A};
+  float* dfv;
+  uint8_t* dfq;
+  uint8_t fq[10];
+  CHECK_HIP(hipMalloc((void**)&dfv, sizeof(fv)));
+  CHECK_HIP(hipMalloc((void**)&dfq, sizeof(fq)));
+  CHECK_HIP(hipMemcpy(dfv, fv, sizeof(fv), hipMemcpyHostToDevice));
+  CHECK_MOE(moe_encode_e4m3(dfv, dfq, 10, stream));
+  CHECK_HIP(hipMemcpyAsync(fq, dfq, sizeof(fq), hipMemcpyDeviceToHost, stream));
+  CHECK_HIP(hipStreamSynchronize(stream));
+  for (int i = 0; i < 10; ++i) {
+    if (fq[i] != fwant[i]) {
+      fprintf(stderr, "moe_encode_e4m3(%a) = 0x%02x, want 0x%02x\n", (double)fv[i], fq[i], fwant[i]);
+      ++fails;
+    }
+  }
+  hipFree(dgx); hipFree(dllws); hipFree(dllx); hipFree(dllsrc); hipFree(dllcnt); hipFree(dllpos); hipFree(dllout);
+  hipFree(dfv); hipFree(dfq);
   hipFree(dx); hipFree(didx); hipFree(dw); hipFree(dtpr); hipFree(dtpe); hipFree(dmask); hipFree(dws);
   hipFree(drecv); hipFree(dsrc); hipFree(dridx); hipFree(drw); hipFree(doffs); hipFree(dsend); hipFree(dn);
   hipFree(dout);
   hipStreamDestroy(stream);
   if (fails) return 1;
-  printf("c abi client: layout, dispatch and combine through the C ABI match (num_recv %d)\n", n);
+  printf("c abi client: layout, dispatch, combine, dispatch backward, low-latency dispatch/combine and "
+         "E4M3 encoding through the C ABI match (num_recv %d)\n", n);
   return 0;
 }
