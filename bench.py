@@ -16,7 +16,10 @@ time.  Graphs remove the host launch gaps that dominate at decode sizes; the
 same K steps as eager launches give ``ms_per_step_eager``, with HIP events
 between the ops for the per-op times (``us_mean``...).  Each op is also timed
 as a graph of back-to-back launches of that op alone (``us_kernel``);
-``layout+dispatch`` is the send side end to end (both ops, same timings).
+``layout+dispatch`` is the send side end to end (both ops, same timings);
+``layout_dispatch_one_call`` is the same work through moe_layout_dispatch (one
+kernel for batches up to 1024 tokens), and ``ms_per_step_one_call`` the step
+replayed with it in place of the two calls.
 
     python bench.py [--steps K] [--warmup W] [--workload prefill|decode|...]
 
@@ -51,6 +54,7 @@ HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 ROTATION_BYTES = 1 << 30  # buffer sets in rotation cover at least this much memory
 OPS = ("layout", "dispatch", "combine")
+FUSED = "layout_dispatch_one_call"  # moe_layout_dispatch: layout and dispatch in one call
 
 
 def log(msg: str) -> None:
@@ -173,6 +177,9 @@ class Workload:
         elif name == "layout+dispatch":  # the end-to-end send side
             self.op_on("layout", s, stream)
             self.op_on("dispatch", s, stream)
+        elif name == FUSED:  # the same outputs from one call (one kernel for small batches)
+            moe.run_layout_dispatch(self.shape, cfg.dispatch_dtype, s["x"], s["idx"], s["w"], s["lay"], s["disp"],
+                                    stream)
         elif name == "dispatch":
             moe.run_dispatch(self.shape, cfg.dispatch_dtype, s["x"], s["idx"], s["w"], s["lay"], s["disp"], stream)
         else:
@@ -201,19 +208,19 @@ class Workload:
         per = {name: [e[i].elapsed_time(e[i + 1]) for e in ev] for i, name in enumerate(OPS)}
         return wall, per
 
-    def time_steps_graph(self, steps: int, warmup: int) -> float:
-        """Wall seconds for `steps` replays of per-set graphs of the whole step."""
+    def time_steps_graph(self, steps: int, warmup: int, ops=OPS) -> float:
+        """Wall seconds for `steps` replays of per-set graphs of the whole step (`ops` in order)."""
         torch = self.torch
         stream = torch.cuda.Stream()
         graphs = []
         with torch.cuda.stream(stream):
             for s in self.sets:
-                for name in OPS:  # warm-up on the capture stream
+                for name in ops:  # warm-up on the capture stream
                     self.op(name, s)
                 torch.cuda.synchronize()
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
-                    for name in OPS:
+                    for name in ops:
                         self.op(name, s)
                 graphs.append(g)
         n = len(graphs)
@@ -693,8 +700,16 @@ def main() -> int:
         per[both] = [a + b for a, b in zip(per["layout"], per["dispatch"])]  # event to event, both ops
         ops = {o: op_summary(wl.bytes[o], per[o], kern[o]) for o in OPS}
         ops[both] = op_summary(wl.bytes["layout"] + wl.bytes["dispatch"], per[both], kern[both])
+        # the send side as one call, and the step built on it (graph replays)
+        wall_one = wl.time_steps_graph(args.steps, args.warmup, ops=(FUSED, "combine"))
+        if not args.no_kernel_timing:
+            us = wl.time_kernels(ops=(FUSED,))[FUSED]
+            b_send = wl.bytes["layout"] + wl.bytes["dispatch"]
+            ops[FUSED] = {"us_kernel": round(us, 3), "bytes": int(b_send),
+                          "GB_per_s_kernel": round(b_send / (us * 1e-6) / 1e9, 2)}
         res = {"cfg": cfg, "n_recv": wl.n_recv, "ops": ops, "ms_per_step": wall * 1e3 / args.steps,
                "ms_per_step_eager": wall_eager * 1e3 / args.steps,
+               "ms_per_step_one_call": wall_one * 1e3 / args.steps,
                "step_bytes": sum(wl.bytes.values()), "sets": len(wl.sets)}
         if name == args.workload and args.cu_sweep:
             res["cu_budget"] = cu_sweep(wl, torch, moe)
@@ -759,6 +774,7 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(main_res["ms_per_step"], 4),
         "ms_per_step_eager": round(main_res["ms_per_step_eager"], 4),
+        "ms_per_step_one_call": round(main_res["ms_per_step_one_call"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -782,6 +798,7 @@ def main() -> int:
                                          f"top-{c2.num_topk} R={c2.num_ranks} {c2.dispatch_dtype} dispatch",
                              "n_recv": sec["n_recv"], "ms_per_step": round(sec["ms_per_step"], 4),
                              "ms_per_step_eager": round(sec["ms_per_step_eager"], 4),
+                             "ms_per_step_one_call": round(sec["ms_per_step_one_call"], 4),
                              "ops": sec["ops"]}
         for key in ("low_latency", "router"):
             if key in sec:

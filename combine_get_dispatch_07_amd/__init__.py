@@ -15,7 +15,7 @@ import torch
 
 from ._lib import (LIB_PATH, MoeError, MoeShape, ll_workspace_bytes, max_recv_rows, moe_combine,  # noqa: F401
                    moe_combine_backward, moe_combine_ll, moe_dispatch, moe_dispatch_backward, moe_dispatch_ll,
-                   moe_encode_e4m3,
+                   moe_encode_e4m3, moe_layout_dispatch,
                    moe_get_dispatch_layout, moe_route_layout, status_string, stream_create_cu_range, stream_destroy,
                    workspace_bytes)
 
@@ -71,6 +71,16 @@ def run_dispatch(shape: MoeShape, dtype: str, x: torch.Tensor, topk_idx: torch.T
     moe_dispatch(shape, dtype, x, topk_idx, topk_w, lay["workspace"], d["recv_x"], d["recv_scales"],
                  d["recv_src_idx"], d["recv_topk_idx"], d["recv_topk_w"], d["rank_offsets"], d["send_row"],
                  d["num_recv"], stream)
+
+
+def run_layout_dispatch(shape: MoeShape, dtype: str, x: torch.Tensor, topk_idx: torch.Tensor,
+                        topk_w: torch.Tensor, lay: Dict[str, torch.Tensor], d: Dict[str, torch.Tensor],
+                        stream=None) -> None:
+    """run_layout then run_dispatch as one call (one kernel for small batches)."""
+    moe_layout_dispatch(shape, dtype, x, topk_idx, topk_w, lay["tokens_per_rank"], lay["tokens_per_expert"],
+                        lay["is_token_in_rank"], lay["workspace"], d["recv_x"], d["recv_scales"], d["recv_src_idx"],
+                        d["recv_topk_idx"], d["recv_topk_w"], d["rank_offsets"], d["send_row"], d["num_recv"],
+                        stream)
 
 
 def alloc_dispatch_ll(shape: MoeShape, dtype: str, device="cuda", capacity: Optional[int] = None

@@ -119,14 +119,13 @@ __device__ __forceinline__ void publish_rank_offsets(const LayoutArgs& a, const 
   if (lane == a.R - 1) a.ws_rank_offsets[a.R] = incl;
 }
 
-// T <= kFusedMaxTokens: one block of ceil(T/64) waves (at least one) does
-// everything in one launch.  Dynamic LDS: hist[E]; static: chunk counts [R][16].
+// The whole layout in one block of at least ceil(T/64) waves (at most 16):
+// thread i owns token i, wave w chunk w; waves beyond the last chunk count
+// nothing.  hist: E ints of LDS.  Returns after wave 0 has published the rank
+// offsets; rank_total then holds the per-rank token counts.
 template <int KI>
-__global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArgs a) {
-  extern __shared__ int hist[];
-  __shared__ int chunk_cnt[kWave * kFusedMaxChunks];
-  __shared__ int wave_cnt[kFusedMaxChunks][kWave];
-  __shared__ int rank_total[kWave];
+__device__ __forceinline__ void layout_one_block(const LayoutArgs& a, int* hist, int* chunk_cnt,
+                                                 int (*wave_cnt)[kWave], int* rank_total) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   for (int e = tid; e < a.E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
@@ -151,6 +150,17 @@ __global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArg
   }
   __syncthreads();
   if (wave == 0) publish_rank_offsets(a, rank_total, lane);
+}
+
+// T <= kFusedMaxTokens: one block of ceil(T/64) waves (at least one) does
+// everything in one launch.  Dynamic LDS: hist[E]; static: chunk counts [R][16].
+template <int KI>
+__global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArgs a) {
+  extern __shared__ int hist[];
+  __shared__ int chunk_cnt[kWave * kFusedMaxChunks];
+  __shared__ int wave_cnt[kFusedMaxChunks][kWave];
+  __shared__ int rank_total[kWave];
+  layout_one_block<KI>(a, hist, chunk_cnt, wave_cnt, rank_total);
 }
 
 // Multi-block path, pass 1: mask rows, token bitmasks, chunk counts, block histograms.

@@ -20,6 +20,7 @@
 #include "layout_kernels.h"
 #include "ll_kernels.h"
 #include "router_kernels.h"
+#include "send_small_kernels.h"
 
 namespace {
 
@@ -127,6 +128,10 @@ static_assert(MOE_BWD_WAVES >= 1 && MOE_BWD_WAVES <= moe::kBwdMaxWaves, "waves p
 #endif
 #ifndef MOE_COMBINE_WAVES_PER_CU
 #define MOE_COMBINE_WAVES_PER_CU 4
+#endif
+// Layout and dispatch in one launch for small batches in moe_layout_dispatch (0: two launches).
+#ifndef MOE_SEND_SMALL
+#define MOE_SEND_SMALL 1
 #endif
 #ifndef MOE_COMBINE_MAX_WAVES_PER_CU
 #define MOE_COMBINE_MAX_WAVES_PER_CU 16
@@ -276,6 +281,168 @@ void launch_router(int T, size_t lds, hipStream_t stream, const moe::RouterArgs&
   }
 }
 
+// Layout arguments after every check moe_get_dispatch_layout makes (shape already checked).
+moe_status layout_args(const moe_shape& s, const int32_t* topk_idx, int32_t* tokens_per_rank,
+                       int32_t* tokens_per_expert, uint8_t* is_token_in_rank, void* workspace, size_t workspace_bytes,
+                       moe::LayoutArgs& a) {
+  const int64_t T = s.num_tokens;
+  if (!present(topk_idx, T) || !present(is_token_in_rank, T) || !tokens_per_rank || !tokens_per_expert ||
+      !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(topk_idx, 4) || !aligned(tokens_per_rank, 4) || !aligned(tokens_per_expert, 4) ||
+      !aligned(workspace, kPlanAlign))
+    return MOE_ERR_INVALID_ARG;
+  const PlanLayout p = plan_layout(s);
+  if (workspace_bytes < p.total) return MOE_ERR_INVALID_ARG;
+
+  char* ws = static_cast<char*>(workspace);
+  a = moe::LayoutArgs{};
+  a.topk_idx = topk_idx;
+  a.tokens_per_rank = tokens_per_rank;
+  a.tokens_per_expert = tokens_per_expert;
+  a.mask = is_token_in_rank;
+  a.token_ranks = reinterpret_cast<uint64_t*>(ws + p.token_ranks);
+  a.chunk_base = reinterpret_cast<int32_t*>(ws + p.chunk_base);
+  a.block_expert = reinterpret_cast<int32_t*>(ws + p.block_expert);
+  a.ws_rank_offsets = reinterpret_cast<int32_t*>(ws + p.rank_offsets);
+  a.rank_magic = rank_magic(s);
+  a.T = s.num_tokens;
+  a.k = s.num_topk;
+  a.E = s.num_experts;
+  a.R = s.num_ranks;
+  a.NC = p.NC;
+  a.NB = p.NB;
+  a.mask_words = (s.num_ranks % 4 == 0 && aligned(is_token_in_rank, 4)) ? 1 : 0;
+  a.ids_vec4 = (s.num_topk % 4 == 0 && aligned(topk_idx, 16)) ? 1 : 0;
+  return MOE_OK;
+}
+
+void launch_layout(const moe::LayoutArgs& a, hipStream_t stream) {
+  const size_t hist_bytes = (size_t)a.E * sizeof(int);
+  const bool narrow = a.k <= 8;  // ids held per lane: 8, else the top-k limit
+  if (a.T <= moe::kFusedMaxTokens) {
+    const int threads = std::max(moe::kWave, (a.T + moe::kWave - 1) / moe::kWave * moe::kWave);
+    if (narrow)
+      hipLaunchKernelGGL(moe::layout_fused_kernel<8>, dim3(1), dim3(threads), hist_bytes, stream, a);
+    else
+      hipLaunchKernelGGL(moe::layout_fused_kernel<moe::kMaxTopk>, dim3(1), dim3(threads), hist_bytes, stream, a);
+  } else {
+    if (narrow)
+      hipLaunchKernelGGL(moe::layout_count_kernel<8>, dim3(a.NB), dim3(moe::kLayoutBlock), hist_bytes, stream, a);
+    else
+      hipLaunchKernelGGL(moe::layout_count_kernel<moe::kMaxTopk>, dim3(a.NB), dim3(moe::kLayoutBlock), hist_bytes,
+                         stream, a);
+    hipLaunchKernelGGL(moe::layout_finalize_kernel, dim3(1), dim3(1024), 0, stream, a);
+  }
+}
+
+// Dispatch arguments after every check moe_dispatch makes (shape already checked); U is the
+// slice width the launch uses.
+moe_status dispatch_args(const moe_shape& s, moe_dtype dtype, const void* x, const int32_t* topk_idx,
+                         const float* topk_w, const void* workspace, size_t workspace_bytes, int32_t recv_capacity,
+                         void* recv_x, float* recv_scales, int32_t* recv_src_idx, int32_t* recv_topk_idx,
+                         float* recv_topk_w, int32_t* rank_offsets, int32_t* send_row, int32_t* num_recv,
+                         moe::DispatchArgs& a, int& U) {
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = dtype == MOE_FP8_E4M3;
+  if (fp8 && s.hidden % moe::kFp8Block != 0) return MOE_ERR_INVALID_ARG;
+  const int64_t T = s.num_tokens, cap = recv_capacity;
+  if (!present(x, T) || !present(topk_idx, T) || !present(topk_w, T) || !present(send_row, T) || !workspace ||
+      !present(recv_x, cap) || !present(recv_src_idx, cap) || !present(recv_topk_idx, cap) ||
+      !present(recv_topk_w, cap) || (fp8 && !present(recv_scales, cap)) || !rank_offsets || !num_recv)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
+      !aligned(workspace, kPlanAlign) || !aligned(recv_src_idx, 4) || !aligned(recv_topk_idx, 4) ||
+      !aligned(recv_topk_w, 4) || !aligned(rank_offsets, 4) || !aligned(send_row, 4) ||
+      !aligned(num_recv, 4) || (fp8 && !aligned(recv_scales, 4)))
+    return MOE_ERR_INVALID_ARG;
+  const PlanLayout p = plan_layout(s);
+  if (workspace_bytes < p.total) return MOE_ERR_INVALID_ARG;
+  if (recv_capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (recv_capacity < s.num_tokens * std::min(s.num_topk, s.num_ranks)) return MOE_ERR_CAPACITY;
+
+  const char* ws = static_cast<const char*>(workspace);
+  a = moe::DispatchArgs{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.token_ranks = reinterpret_cast<const uint64_t*>(ws + p.token_ranks);
+  a.chunk_base = reinterpret_cast<const int32_t*>(ws + p.chunk_base);
+  a.ws_rank_offsets = reinterpret_cast<const int32_t*>(ws + p.rank_offsets);
+  a.recv_x = recv_x;
+  a.recv_scales = recv_scales;
+  a.recv_src_idx = recv_src_idx;
+  a.recv_topk_idx = recv_topk_idx;
+  a.recv_topk_w = recv_topk_w;
+  a.rank_offsets = rank_offsets;
+  a.send_row = send_row;
+  a.num_recv = num_recv;
+  a.rank_magic = rank_magic(s);
+  a.rank_bits = s.num_ranks == 64 ? ~0ull : ((1ull << s.num_ranks) - 1);
+  a.T = s.num_tokens;
+  a.H = s.hidden;
+  a.H8 = s.hidden / 8;
+  a.k = s.num_topk;
+  a.E = s.num_experts;
+  a.R = s.num_ranks;
+  a.L = s.num_experts / s.num_ranks;
+  a.NC = p.NC;
+  a.capacity = recv_capacity;
+#ifdef MOE_FORCE_DISPATCH_U
+  U = MOE_FORCE_DISPATCH_U;
+#else
+  U = pick_dispatch_chunks_per_lane(s.num_tokens, a.H8, fp8);
+#endif
+  const int groups = (a.H8 + moe::kWave - 1) / moe::kWave;
+  a.slices = (groups + U - 1) / U;
+  if ((int64_t)s.num_tokens * a.slices > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  a.items = s.num_tokens * a.slices;
+  return MOE_OK;
+}
+
+void launch_dispatch_args(const moe::DispatchArgs& a, int U, bool fp8, hipStream_t stream) {
+  const int waves_per_block = moe::kDispatchBlock / moe::kWave;
+  const dim3 grid(std::max(1, (a.items + waves_per_block - 1) / waves_per_block));
+  if (fp8)
+    launch_dispatch<true>(U, grid, stream, a);
+  else
+    launch_dispatch<false>(U, grid, stream, a);
+}
+
+template <int U>
+void launch_send_small_t(bool fp8, bool narrow, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                         const moe::SendSmallArgs& a) {
+  if (fp8 && narrow)
+    hipLaunchKernelGGL((moe::send_small_kernel<U, true, 8>), grid, block, lds, stream, a);
+  else if (fp8)
+    hipLaunchKernelGGL((moe::send_small_kernel<U, true, moe::kMaxTopk>), grid, block, lds, stream, a);
+  else if (narrow)
+    hipLaunchKernelGGL((moe::send_small_kernel<U, false, 8>), grid, block, lds, stream, a);
+  else
+    hipLaunchKernelGGL((moe::send_small_kernel<U, false, moe::kMaxTopk>), grid, block, lds, stream, a);
+}
+
+// Layout and dispatch in one launch (T <= 1024, hidden <= 16384): returns false when the
+// batch is outside that range and nothing was launched.
+bool launch_send_small(const moe::LayoutArgs& lay, const moe::DispatchArgs& d, bool fp8, hipStream_t stream) {
+  if (!MOE_SEND_SMALL || d.T > moe::kSendSmallMaxTokens) return false;
+  const int groups = (d.H8 + moe::kWave - 1) / moe::kWave;
+  const int U = groups <= moe::kSendSmallMaxWaves ? 1 : groups <= 2 * moe::kSendSmallMaxWaves ? 2 : 0;
+  if (U == 0) return false;
+  moe::SendSmallArgs a{lay, d};
+  a.d.slices = (groups + U - 1) / U;
+  a.d.items = d.T * a.d.slices;
+  const int waves = std::max({a.d.slices, (d.T + moe::kWave - 1) / moe::kWave, 1});
+  const dim3 grid(d.T + 1), block(waves * moe::kWave);
+  const size_t lds = (size_t)lay.E * sizeof(int);
+  const bool narrow = d.k <= 8;  // ids held per lane: 8, else the top-k limit
+  if (U == 1)
+    launch_send_small_t<1>(fp8, narrow, grid, block, lds, stream, a);
+  else
+    launch_send_small_t<2>(fp8, narrow, grid, block, lds, stream, a);
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -307,53 +474,11 @@ moe_status moe_get_dispatch_layout(const moe_shape* shape, const int32_t* topk_i
                                    size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  const moe_shape s = *shape;
-  const int64_t T = s.num_tokens;
-  if (!present(topk_idx, T) || !present(is_token_in_rank, T) || !tokens_per_rank || !tokens_per_expert ||
-      !workspace)
-    return MOE_ERR_INVALID_ARG;
-  if (!aligned(topk_idx, 4) || !aligned(tokens_per_rank, 4) || !aligned(tokens_per_expert, 4) ||
-      !aligned(workspace, kPlanAlign))
-    return MOE_ERR_INVALID_ARG;
-  const PlanLayout p = plan_layout(s);
-  if (workspace_bytes < p.total) return MOE_ERR_INVALID_ARG;
-
-  char* ws = static_cast<char*>(workspace);
-  moe::LayoutArgs a{};
-  a.topk_idx = topk_idx;
-  a.tokens_per_rank = tokens_per_rank;
-  a.tokens_per_expert = tokens_per_expert;
-  a.mask = is_token_in_rank;
-  a.token_ranks = reinterpret_cast<uint64_t*>(ws + p.token_ranks);
-  a.chunk_base = reinterpret_cast<int32_t*>(ws + p.chunk_base);
-  a.block_expert = reinterpret_cast<int32_t*>(ws + p.block_expert);
-  a.ws_rank_offsets = reinterpret_cast<int32_t*>(ws + p.rank_offsets);
-  a.rank_magic = rank_magic(s);
-  a.T = s.num_tokens;
-  a.k = s.num_topk;
-  a.E = s.num_experts;
-  a.R = s.num_ranks;
-  a.NC = p.NC;
-  a.NB = p.NB;
-  a.mask_words = (s.num_ranks % 4 == 0 && aligned(is_token_in_rank, 4)) ? 1 : 0;
-  a.ids_vec4 = (s.num_topk % 4 == 0 && aligned(topk_idx, 16)) ? 1 : 0;
-  const size_t hist_bytes = (size_t)s.num_experts * sizeof(int);
-
-  const bool narrow = s.num_topk <= 8;  // ids held per lane: 8, else the top-k limit
-  if (s.num_tokens <= moe::kFusedMaxTokens) {
-    const int threads = std::max(moe::kWave, (s.num_tokens + moe::kWave - 1) / moe::kWave * moe::kWave);
-    if (narrow)
-      hipLaunchKernelGGL(moe::layout_fused_kernel<8>, dim3(1), dim3(threads), hist_bytes, stream, a);
-    else
-      hipLaunchKernelGGL(moe::layout_fused_kernel<moe::kMaxTopk>, dim3(1), dim3(threads), hist_bytes, stream, a);
-  } else {
-    if (narrow)
-      hipLaunchKernelGGL(moe::layout_count_kernel<8>, dim3(p.NB), dim3(moe::kLayoutBlock), hist_bytes, stream, a);
-    else
-      hipLaunchKernelGGL(moe::layout_count_kernel<moe::kMaxTopk>, dim3(p.NB), dim3(moe::kLayoutBlock), hist_bytes,
-                         stream, a);
-    hipLaunchKernelGGL(moe::layout_finalize_kernel, dim3(1), dim3(1024), 0, stream, a);
-  }
+  moe::LayoutArgs a;
+  st = layout_args(*shape, topk_idx, tokens_per_rank, tokens_per_expert, is_token_in_rank, workspace,
+                   workspace_bytes, a);
+  if (st != MOE_OK) return st;
+  launch_layout(a, stream);
   return last_launch_status();
 }
 
@@ -427,67 +552,37 @@ moe_status moe_dispatch(const moe_shape* shape, moe_dtype dtype, const void* x,
                         int32_t* num_recv, hipStream_t stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  const moe_shape s = *shape;
-  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
-  const bool fp8 = dtype == MOE_FP8_E4M3;
-  if (fp8 && s.hidden % moe::kFp8Block != 0) return MOE_ERR_INVALID_ARG;
-  const int64_t T = s.num_tokens, cap = recv_capacity;
-  if (!present(x, T) || !present(topk_idx, T) || !present(topk_w, T) || !present(send_row, T) || !workspace ||
-      !present(recv_x, cap) || !present(recv_src_idx, cap) || !present(recv_topk_idx, cap) ||
-      !present(recv_topk_w, cap) || (fp8 && !present(recv_scales, cap)) || !rank_offsets || !num_recv)
-    return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
-      !aligned(workspace, kPlanAlign) || !aligned(recv_src_idx, 4) || !aligned(recv_topk_idx, 4) ||
-      !aligned(recv_topk_w, 4) || !aligned(rank_offsets, 4) || !aligned(send_row, 4) ||
-      !aligned(num_recv, 4) || (fp8 && !aligned(recv_scales, 4)))
-    return MOE_ERR_INVALID_ARG;
-  const PlanLayout p = plan_layout(s);
-  if (workspace_bytes < p.total) return MOE_ERR_INVALID_ARG;
-  if (recv_capacity < 0) return MOE_ERR_INVALID_ARG;
-  if (recv_capacity < s.num_tokens * std::min(s.num_topk, s.num_ranks)) return MOE_ERR_CAPACITY;
+  moe::DispatchArgs a;
+  int U = 1;
+  st = dispatch_args(*shape, dtype, x, topk_idx, topk_w, workspace, workspace_bytes, recv_capacity, recv_x,
+                     recv_scales, recv_src_idx, recv_topk_idx, recv_topk_w, rank_offsets, send_row, num_recv, a, U);
+  if (st != MOE_OK) return st;
+  launch_dispatch_args(a, U, dtype == MOE_FP8_E4M3, stream);
+  return last_launch_status();
+}
 
-  const char* ws = static_cast<const char*>(workspace);
-  moe::DispatchArgs a{};
-  a.x = static_cast<const uint16_t*>(x);
-  a.topk_idx = topk_idx;
-  a.topk_w = topk_w;
-  a.token_ranks = reinterpret_cast<const uint64_t*>(ws + p.token_ranks);
-  a.chunk_base = reinterpret_cast<const int32_t*>(ws + p.chunk_base);
-  a.ws_rank_offsets = reinterpret_cast<const int32_t*>(ws + p.rank_offsets);
-  a.recv_x = recv_x;
-  a.recv_scales = recv_scales;
-  a.recv_src_idx = recv_src_idx;
-  a.recv_topk_idx = recv_topk_idx;
-  a.recv_topk_w = recv_topk_w;
-  a.rank_offsets = rank_offsets;
-  a.send_row = send_row;
-  a.num_recv = num_recv;
-  a.rank_magic = rank_magic(s);
-  a.rank_bits = s.num_ranks == 64 ? ~0ull : ((1ull << s.num_ranks) - 1);
-  a.T = s.num_tokens;
-  a.H = s.hidden;
-  a.H8 = s.hidden / 8;
-  a.k = s.num_topk;
-  a.E = s.num_experts;
-  a.R = s.num_ranks;
-  a.L = s.num_experts / s.num_ranks;
-  a.NC = p.NC;
-  a.capacity = recv_capacity;
-#ifdef MOE_FORCE_DISPATCH_U
-  const int U = MOE_FORCE_DISPATCH_U;
-#else
-  const int U = pick_dispatch_chunks_per_lane(s.num_tokens, a.H8, fp8);
-#endif
-  const int groups = (a.H8 + moe::kWave - 1) / moe::kWave;
-  a.slices = (groups + U - 1) / U;
-  if ((int64_t)s.num_tokens * a.slices > INT32_MAX) return MOE_ERR_UNSUPPORTED;
-  a.items = s.num_tokens * a.slices;
-  const int waves_per_block = moe::kDispatchBlock / moe::kWave;
-  const dim3 grid(std::max(1, (a.items + waves_per_block - 1) / waves_per_block));
-  if (fp8)
-    launch_dispatch<true>(U, grid, stream, a);
-  else
-    launch_dispatch<false>(U, grid, stream, a);
+moe_status moe_layout_dispatch(const moe_shape* shape, moe_dtype dtype, const void* x, const int32_t* topk_idx,
+                               const float* topk_w, int32_t* tokens_per_rank, int32_t* tokens_per_expert,
+                               uint8_t* is_token_in_rank, void* workspace, size_t workspace_bytes,
+                               int32_t recv_capacity, void* recv_x, float* recv_scales, int32_t* recv_src_idx,
+                               int32_t* recv_topk_idx, float* recv_topk_w, int32_t* rank_offsets,
+                               int32_t* send_row, int32_t* num_recv, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  moe::LayoutArgs lay;
+  st = layout_args(*shape, topk_idx, tokens_per_rank, tokens_per_expert, is_token_in_rank, workspace,
+                   workspace_bytes, lay);
+  if (st != MOE_OK) return st;
+  moe::DispatchArgs d;
+  int U = 1;
+  st = dispatch_args(*shape, dtype, x, topk_idx, topk_w, workspace, workspace_bytes, recv_capacity, recv_x,
+                     recv_scales, recv_src_idx, recv_topk_idx, recv_topk_w, rank_offsets, send_row, num_recv, d, U);
+  if (st != MOE_OK) return st;
+  const bool fp8 = dtype == MOE_FP8_E4M3;
+  if (!launch_send_small(lay, d, fp8, stream)) {
+    launch_layout(lay, stream);
+    launch_dispatch_args(d, U, fp8, stream);
+  }
   return last_launch_status();
 }
 

@@ -182,6 +182,26 @@ moe_status moe_dispatch(const moe_shape* shape, moe_dtype dtype, const void* x,
                         float* recv_topk_w, int32_t* rank_offsets, int32_t* send_row,
                         int32_t* num_recv, hipStream_t stream);
 
+/* Layout and dispatch in one call.  [overlap notes, 节点内通信: filtered send;
+ * rocSHMEM notes 3.2: rows packed into a preallocated receive buffer.]
+ *
+ * Writes everything moe_get_dispatch_layout and then moe_dispatch write for the
+ * same arguments -- tokens_per_rank, tokens_per_expert, is_token_in_rank, the
+ * plan in `workspace` (so that a later moe_dispatch with this workspace is
+ * valid), the receive rows, their metadata, rank_offsets, send_row and
+ * num_recv -- with identical values.  Arguments, limits and errors are the
+ * union of the two calls'.  For T <= 1024 and hidden <= 16384 one kernel does
+ * both steps (every block recounts the batch's rank bitmasks, so no launch
+ * boundary separates the prefix sums from the packing); otherwise the two
+ * calls' launches run back to back.
+ */
+moe_status moe_layout_dispatch(const moe_shape* shape, moe_dtype dtype, const void* x, const int32_t* topk_idx,
+                               const float* topk_w, int32_t* tokens_per_rank, int32_t* tokens_per_expert,
+                               uint8_t* is_token_in_rank, void* workspace, size_t workspace_bytes,
+                               int32_t recv_capacity, void* recv_x, float* recv_scales, int32_t* recv_src_idx,
+                               int32_t* recv_topk_idx, float* recv_topk_w, int32_t* rank_offsets,
+                               int32_t* send_row, int32_t* num_recv, hipStream_t stream);
+
 /* The E4M3 rounding the FP8 dispatch applies to x / s, on its own.
  * [overlap notes, 节点内通信: FP8 transport.]
  *

@@ -171,3 +171,21 @@ def test_encode_e4m3_rejections():
     assert enc(None, A, 4, None) == INVALID
     assert enc(A, None, 4, None) == INVALID
     assert enc(None, None, 0, None) == OK  # nothing to launch
+
+
+def test_layout_dispatch_rejections():
+    """The union of the layout's and the dispatch's checks, before any launch."""
+    fn = L.lib.moe_layout_dispatch
+    s = shape()
+    cap = s.num_tokens * min(s.num_topk, s.num_ranks)
+
+    def call(dtype=0, ws=A, ws_bytes=1 << 30, cap_=cap, mask=A, x=A, scales=A):
+        return fn(ctypes.byref(s), dtype, x, A, A, A, A, mask, ws, ws_bytes, cap_, A, scales, A, A, A, A, A, A, None)
+
+    assert call(dtype=7) == INVALID
+    assert call(cap_=cap - 1) == CAPACITY
+    assert call(ws_bytes=1) == INVALID
+    assert call(mask=None) == INVALID  # a layout output missing
+    assert call(x=A + 2) == INVALID  # misaligned x
+    assert call(dtype=1, scales=None) == INVALID  # FP8 needs scales
+    assert fn(None, 0, A, A, A, A, A, A, A, 1 << 30, cap, A, A, A, A, A, A, A, A, None) == INVALID

@@ -1,0 +1,130 @@
+"""moe_layout_dispatch (layout and dispatch in one call; one kernel for T <= 1024 and hidden <= 16384)
+against the two separate calls and against the oracle.
+
+Bar: every output of moe_get_dispatch_layout + moe_dispatch bit-identical (counts, mask, rank
+offsets, send_row, num_recv, receive rows, FP8 scales, row metadata), rows at or beyond num_recv
+untouched, and the plan left in the workspace valid: moe_dispatch run again from it reproduces the
+receive buffers.  Cases cover the one-kernel form (both slice widths, 8 and 32 ids per lane, one to
+sixteen 64-token batches) and the fallback to two launches.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _bufs(moe, shape, dtype, cap):
+    from tests.gpu_harness import _poison
+    lay, d = moe.alloc_layout(shape), moe.alloc_dispatch(shape, dtype, capacity=cap)
+    _poison(lay)
+    _poison(d)
+    return lay, d
+
+
+def _host(lay, d):
+    out = {k: v.cpu().numpy().copy() for k, v in lay.items() if k != "workspace"}
+    out.update({k: (v.view(torch.uint8) if v.dtype == torch.bfloat16 else v).cpu().numpy().copy()
+                for k, v in d.items() if v is not None})
+    return out
+
+
+def run_fused_case(x, idx, w, E, R, dtype):
+    import combine_get_dispatch_07_amd as moe
+    from tests.gpu_harness import to_dev_bf16
+
+    T, H = x.shape
+    k = idx.shape[1]
+    print(f"[case] layout_dispatch T={T} H={H} E={E} k={k} R={R} {dtype}", flush=True)
+    shape = moe.MoeShape(T, H, k, E, R)
+    xd = to_dev_bf16(x) if T else torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
+    w_d = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).cuda()
+    cap = moe.max_recv_rows(shape) + 3  # three guard rows
+
+    lay_a, d_a = _bufs(moe, shape, dtype, cap)  # the separate calls
+    moe.run_layout(shape, idx_d, lay_a)
+    moe.run_dispatch(shape, dtype, xd, idx_d, w_d, lay_a, d_a)
+    lay_b, d_b = _bufs(moe, shape, dtype, cap)  # one call
+    moe.run_layout_dispatch(shape, dtype, xd, idx_d, w_d, lay_b, d_b)
+    torch.cuda.synchronize()
+    a, b = _host(lay_a, d_a), _host(lay_b, d_b)
+    n = int(a["num_recv"][0])
+    for key in a:
+        va, vb = a[key], b[key]
+        assert va.shape == vb.shape, key
+        assert np.array_equal(va.view(np.uint8), vb.view(np.uint8)), key  # guard rows included
+
+    # the plan in the fused call's workspace drives moe_dispatch to the same receive buffers
+    _, d_c = _bufs(moe, shape, dtype, cap)
+    moe.run_dispatch(shape, dtype, xd, idx_d, w_d, lay_b, d_c)
+    torch.cuda.synchronize()
+    c = _host({}, d_c)
+    for key in c:
+        assert np.array_equal(c[key].view(np.uint8), b[key].view(np.uint8)), f"plan: {key}"
+
+    if T == 0:
+        assert n == 0 and not b["tokens_per_rank"].any() and not b["tokens_per_expert"].any()
+        return
+    ref = O.run_all(x, idx, w, E, R, dtype)  # and the oracle
+    assert n == int(ref["num_recv"])
+    for key in ("tokens_per_rank", "tokens_per_expert", "is_token_in_rank", "rank_offsets", "send_row"):
+        assert np.array_equal(b[key], ref[key]), key
+    for key in ("recv_src_idx", "recv_topk_idx"):
+        assert np.array_equal(b[key][:n], ref[key]), key
+    assert np.array_equal(b["recv_topk_w"][:n].view(np.uint32), ref["recv_topk_w"].view(np.uint32))
+    assert np.array_equal(b["recv_x"][:n].reshape(ref["recv_x"].shape[0], -1).view(np.uint8),
+                          ref["recv_x"].reshape(n, -1).view(np.uint8))
+    if dtype == "fp8":
+        assert np.array_equal(b["recv_scales"][:n].view(np.uint32), ref["recv_scales"].view(np.uint32))
+
+
+def test_decode_workload():
+    cfg = W.CONFIG_BY_NAME["decode"]
+    d = W.make_inputs(cfg)
+    run_fused_case(d["x"], d["topk_idx"], d["topk_w"], cfg.num_experts, cfg.num_ranks, cfg.dispatch_dtype)
+
+
+def test_tiny_workload():
+    cfg = W.CONFIG_BY_NAME["tiny"]
+    d = W.make_inputs(cfg)
+    run_fused_case(d["x"], d["topk_idx"], d["topk_w"], cfg.num_experts, cfg.num_ranks, cfg.dispatch_dtype)
+
+
+CASES = [
+    # name, seed, T, H, E, k, R, dtype, invalid_frac
+    ("single_token", 1, 1, 256, 16, 4, 4, "bf16", 0.0),
+    ("limit_1024", 2, 1024, 512, 64, 6, 16, "fp8", 0.1),         # sixteen batches, one kernel
+    ("fallback_1025", 3, 1025, 256, 32, 4, 8, "bf16", 0.05),     # two launches
+    ("max_limits", 4, 300, 256, 4096, 32, 64, "fp8", 0.1),       # 32 ids per lane, 64 ranks
+    ("mostly_invalid", 5, 200, 256, 16, 4, 4, "bf16", 0.7),
+    ("ragged_hidden", 6, 129, 136, 32, 4, 8, "bf16", 0.0),
+    ("two_groups_per_wave", 7, 100, 16384, 64, 8, 8, "fp8", 0.0),  # 32 groups: U = 2
+    ("fallback_wide", 8, 64, 16896, 16, 4, 4, "bf16", 0.1),       # 33 groups: two launches
+    ("one_rank", 9, 77, 256, 8, 2, 1, "bf16", 0.0),
+    ("R_not_multiple_of_4", 10, 333, 256, 30, 5, 6, "fp8", 0.1),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_layout_dispatch_edges(case):
+    name, seed, T, H, E, k, R, dtype, inv = case
+    d = W.random_case(seed, T, H, E, k, R, invalid_frac=inv)
+    idx = d["topk_idx"].copy()
+    if T > 3:
+        idx[2, :2] = max(int(idx[2, 0]), 0)  # one token names an expert twice
+    run_fused_case(d["x"], idx, d["topk_w"], E, R, dtype)
+
+
+def test_empty_batch():
+    x = np.zeros((0, 256), np.uint16)
+    run_fused_case(x, np.zeros((0, 4), np.int32), np.zeros((0, 4), np.float32), 16, 4, "bf16")
