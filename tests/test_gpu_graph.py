@@ -179,3 +179,32 @@ def test_graph_replays_backward():
         moe.moe_dispatch_backward(shape, y, idx, d["send_row"], grad_x, grad_recv_w, grad_topk_w)
 
     _replay_check(step, [grad_y, grad_w, grad_x, grad_topk_w], "backward")
+
+
+def test_graph_replays_one_call_send_side():
+    """moe_layout_dispatch (one kernel at decode size) + moe_combine in a graph."""
+    import combine_get_dispatch_07_amd as moe
+    from tests.gpu_harness import to_dev_bf16
+
+    cfg = W.CONFIG_BY_NAME["decode"]
+    print("[case] graph one-call send side, decode", flush=True)
+    shape = moe.MoeShape(cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks)
+    inp = W.make_inputs(cfg)
+    x = to_dev_bf16(inp["x"])
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    w = torch.from_numpy(inp["topk_w"]).cuda()
+    lay, d, out = _buffers(moe, shape, "fp8", False)
+    y = to_dev_bf16(W.draw_expert_outputs(np.random.default_rng(5), shape.num_tokens * min(shape.num_topk,
+                                                                                              shape.num_ranks),
+                                          shape.hidden))
+
+    def step():
+        moe.run_layout_dispatch(shape, "fp8", x, idx, w, lay, d)
+        moe.moe_combine(shape, y, idx, w, d["send_row"], out)
+
+    step()
+    torch.cuda.synchronize()
+    n = int(d["num_recv"].item())  # receive rows at or beyond n are not written
+    outputs = [lay["tokens_per_rank"], lay["tokens_per_expert"], lay["is_token_in_rank"], d["rank_offsets"],
+               d["send_row"], d["num_recv"], d["recv_src_idx"][:n], d["recv_x"][:n], d["recv_scales"][:n], out]
+    _replay_check(step, outputs, "one-call send side")
