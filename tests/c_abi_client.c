@@ -9,7 +9,8 @@
  *     weight-1 slot contributes x exactly and the weight-0 slot adds +0 (both layouts);
  *   - the per-rank and per-expert counts follow from the routing by hand;
  *   - the dispatch backward of the received rows is x times the number of distinct ranks;
- *   - E4M3 codes of exactly representable values, ties and signed zero are known.
+ *   - E4M3 codes of exactly representable values, ties and signed zero are known;
+ *   - layout and dispatch as one call (moe_layout_dispatch) give the two calls' rows and handle.
  * Exit status 0 on success; prints what failed otherwise.
  */
 #include <stdint.h>
@@ -176,6 +177,43 @@ int main(void) {
     ++fails;
   }
 
+  /* layout and dispatch as one call: the same counts, rows and handle as the two calls above */
+  {
+    int32_t *tpr2, *tpe2, *src2, *ridx2, *offs2, *send2, *n2;
+    uint8_t* mask2;
+    uint16_t* recv2;
+    float* rw2;
+    void* ws2;
+    CHECK_HIP(hipMalloc((void**)&tpr2, R * sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&tpe2, E * sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&mask2, T * R));
+    CHECK_HIP(hipMalloc(&ws2, ws_bytes));
+    CHECK_HIP(hipMalloc((void**)&recv2, (size_t)cap * H * sizeof(uint16_t)));
+    CHECK_HIP(hipMalloc((void**)&src2, cap * sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&ridx2, (size_t)cap * K * sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&rw2, (size_t)cap * K * sizeof(float)));
+    CHECK_HIP(hipMalloc((void**)&offs2, (R + 1) * sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&send2, T * R * sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&n2, sizeof(int32_t)));
+    CHECK_MOE(moe_layout_dispatch(&shape, MOE_BF16, dx, didx, dw, tpr2, tpe2, mask2, ws2, ws_bytes, cap, recv2, NULL,
+                                  src2, ridx2, rw2, offs2, send2, n2, stream));
+    static int32_t sa[T * R], sb[T * R];
+    static uint16_t ra[T * 2 * H], rb[T * 2 * H];
+    int32_t nb = -1;
+    CHECK_HIP(hipMemcpyAsync(sa, dsend, sizeof(sa), hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipMemcpyAsync(sb, send2, sizeof(sb), hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipMemcpyAsync(ra, drecv, (size_t)n * H * sizeof(uint16_t), hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipMemcpyAsync(rb, recv2, (size_t)n * H * sizeof(uint16_t), hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipMemcpyAsync(&nb, n2, sizeof(nb), hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    if (nb != n || memcmp(sa, sb, sizeof(sa)) != 0 || memcmp(ra, rb, (size_t)n * H * sizeof(uint16_t)) != 0) {
+      fprintf(stderr, "moe_layout_dispatch differs from the two calls (num_recv %d vs %d)\n", nb, n);
+      ++fails;
+    }
+    hipFree(tpr2); hipFree(tpe2); hipFree(mask2); hipFree(ws2); hipFree(recv2); hipFree(src2); hipFree(ridx2);
+    hipFree(rw2); hipFree(offs2); hipFree(send2); hipFree(n2);
+  }
+
   /* the E4M3 rounding on its own: exact values, ties to even, signed zero, the largest code */
   const float fv[10] = {0.0f, -0.0f, 1.0f, -2.0f, 448.0f, 0x1p-9f, 0x1p-10f, 0x3p-10f, 1.0625f, 1.1875f};
   const uint8_t fwant[10] = {0x00, 0x80, 0x38, 0xC0, 0x7E, 0x01, 0x00, 0x02, 0x38, 0x3A};
@@ -201,7 +239,7 @@ int main(void) {
   hipFree(dout);
   hipStreamDestroy(stream);
   if (fails) return 1;
-  printf("c abi client: layout, dispatch, combine, dispatch backward, low-latency dispatch/combine and "
-         "E4M3 encoding through the C ABI match (num_recv %d)\n", n);
+  printf("c abi client: layout, dispatch, one-call layout+dispatch, combine, dispatch backward, low-latency "
+         "dispatch/combine and E4M3 encoding through the C ABI match (num_recv %d)\n", n);
   return 0;
 }
