@@ -8,10 +8,10 @@ the timed region.  Several independent buffer sets (identical inputs) are
 used in rotation, sized so that one set's data has left the 256 MB
 last-level cache before it is used again.
 
-Timed region (``ms_per_step``, ``value``): K steps (default 200, after 100 warm-up steps), each the replay of a HIP
-graph of layout -> dispatch -> combine captured on one buffer set (one graph
-per set, sets in rotation; every step runs all three kernels), bracketed by a
-synchronize on both sides.  ``value`` = whole-step algorithmic bytes / step
+Timed region (``ms_per_step``, ``value``): exactly K steps (default 200, after
+100 warm-up steps) of layout -> dispatch -> combine, replayed from HIP graphs
+that each hold 16 consecutive steps on the buffer sets in rotation (every step
+runs all three kernels), bracketed by a synchronize on both sides.  ``value`` = whole-step algorithmic bytes / step
 time.  Graphs remove the host launch gaps that dominate at decode sizes; the
 same K steps as eager launches give ``ms_per_step_eager``, with HIP events
 between the ops for the per-op times (``us_mean``...).  Each op is also timed
@@ -55,6 +55,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 ROTATION_BYTES = 1 << 30  # buffer sets in rotation cover at least this much memory
 OPS = ("layout", "dispatch", "combine")
 FUSED = "layout_dispatch_one_call"  # moe_layout_dispatch: layout and dispatch in one call
+STEPS_PER_GRAPH = 16  # consecutive steps captured in one graph for the timed replays
 
 
 def log(msg: str) -> None:
@@ -208,31 +209,41 @@ class Workload:
         per = {name: [e[i].elapsed_time(e[i + 1]) for e in ev] for i, name in enumerate(OPS)}
         return wall, per
 
-    def time_steps_graph(self, steps: int, warmup: int, ops=OPS) -> float:
-        """Wall seconds for `steps` replays of per-set graphs of the whole step (`ops` in order)."""
+    def time_steps_graph(self, steps: int, warmup: int, ops=OPS, per_graph: int = STEPS_PER_GRAPH) -> float:
+        """Wall seconds for exactly `steps` steps (`ops` in order), replayed from graphs that each hold
+        `per_graph` consecutive steps on the buffer sets in rotation (one more graph holds the
+        remainder).  Several steps per replay keep the host's per-replay cost from setting the pace
+        of short (decode-sized) steps."""
         torch = self.torch
         stream = torch.cuda.Stream()
-        graphs = []
+        n = len(self.sets)
+
+        def capture(count):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(count):
+                    for name in ops:
+                        self.op(name, self.sets[i % n])
+            return g
+
         with torch.cuda.stream(stream):
             for s in self.sets:
                 for name in ops:  # warm-up on the capture stream
                     self.op(name, s)
-                torch.cuda.synchronize()
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    for name in ops:
-                        self.op(name, s)
-                graphs.append(g)
-        n = len(graphs)
-        for i in range(warmup):
-            graphs[i % n].replay()
+            torch.cuda.synchronize()
+            full = capture(per_graph)
+            tail = capture(steps % per_graph) if steps % per_graph else None
+        for _ in range(-(-warmup // per_graph)):
+            full.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            graphs[i % n].replay()
+        for _ in range(steps // per_graph):
+            full.replay()
+        if tail is not None:
+            tail.replay()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        del graphs
+        del full, tail
         return wall
 
     def time_kernels(self, reps: int = 20, repeats: int = 5, ops=OPS) -> dict:
