@@ -164,8 +164,8 @@ class Workload:
     def _tensors(self, s):
         for v in s.values():
             if isinstance(v, dict):
-                yield from (t for t in v.values() if t is not None)
-            else:
+                yield from (t for t in v.values() if isinstance(t, self.torch.Tensor))
+            elif isinstance(v, self.torch.Tensor):
                 yield v
 
     def op(self, name, s):
@@ -173,18 +173,24 @@ class Workload:
 
     def op_on(self, name, s, stream):
         moe, cfg = self.moe, self.cfg
-        if name == "layout":
-            moe.run_layout(self.shape, s["idx"], s["lay"], stream)
-        elif name == "layout+dispatch":  # the end-to-end send side
+        if name == "layout+dispatch":  # the end-to-end send side
             self.op_on("layout", s, stream)
             self.op_on("dispatch", s, stream)
-        elif name == FUSED:  # the same outputs from one call (one kernel for small batches)
-            moe.run_layout_dispatch(self.shape, cfg.dispatch_dtype, s["x"], s["idx"], s["w"], s["lay"], s["disp"],
-                                    stream)
-        elif name == "dispatch":
-            moe.run_dispatch(self.shape, cfg.dispatch_dtype, s["x"], s["idx"], s["w"], s["lay"], s["disp"], stream)
-        else:
-            moe.moe_combine(self.shape, s["y"], s["idx"], s["w"], s["disp"]["send_row"], s["out"], stream)
+            return
+        calls = s.setdefault("calls", {})  # each op's arguments checked once per buffer set
+        if name not in calls:
+            if name == "layout":
+                calls[name] = moe.prepare_layout(self.shape, s["idx"], s["lay"])
+            elif name == FUSED:  # the same outputs from one call (one kernel for small batches)
+                calls[name] = moe.prepare_layout_dispatch(self.shape, cfg.dispatch_dtype, s["x"], s["idx"], s["w"],
+                                                          s["lay"], s["disp"])
+            elif name == "dispatch":
+                calls[name] = moe.prepare_dispatch(self.shape, cfg.dispatch_dtype, s["x"], s["idx"], s["w"],
+                                                   s["lay"], s["disp"])
+            else:
+                calls[name] = moe.prepare_combine(self.shape, s["y"], s["idx"], s["w"], s["disp"]["send_row"],
+                                                  s["out"])
+        calls[name](stream)
 
     def time_steps(self, steps: int, warmup: int):
         torch = self.torch

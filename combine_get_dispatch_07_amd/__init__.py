@@ -15,7 +15,7 @@ import torch
 
 from ._lib import (LIB_PATH, MoeError, MoeShape, ll_workspace_bytes, max_recv_rows, moe_combine,  # noqa: F401
                    moe_combine_backward, moe_combine_ll, moe_dispatch, moe_dispatch_backward, moe_dispatch_ll,
-                   moe_encode_e4m3, moe_layout_dispatch,
+                   moe_encode_e4m3, moe_layout_dispatch, Prepared,
                    moe_get_dispatch_layout, moe_route_layout, status_string, stream_create_cu_range, stream_destroy,
                    workspace_bytes)
 
@@ -81,6 +81,35 @@ def run_layout_dispatch(shape: MoeShape, dtype: str, x: torch.Tensor, topk_idx: 
                         lay["is_token_in_rank"], lay["workspace"], d["recv_x"], d["recv_scales"], d["recv_src_idx"],
                         d["recv_topk_idx"], d["recv_topk_w"], d["rank_offsets"], d["send_row"], d["num_recv"],
                         stream)
+
+
+def prepare_layout(shape: MoeShape, topk_idx: torch.Tensor, lay: Dict[str, torch.Tensor]) -> Prepared:
+    """run_layout with its arguments checked once: returns a call taking only the stream."""
+    return moe_get_dispatch_layout(shape, topk_idx, lay["tokens_per_rank"], lay["tokens_per_expert"],
+                                   lay["is_token_in_rank"], lay["workspace"], prepare=True)
+
+
+def prepare_dispatch(shape: MoeShape, dtype: str, x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                     lay: Dict[str, torch.Tensor], d: Dict[str, torch.Tensor]) -> Prepared:
+    """run_dispatch with its arguments checked once."""
+    return moe_dispatch(shape, dtype, x, topk_idx, topk_w, lay["workspace"], d["recv_x"], d["recv_scales"],
+                        d["recv_src_idx"], d["recv_topk_idx"], d["recv_topk_w"], d["rank_offsets"], d["send_row"],
+                        d["num_recv"], prepare=True)
+
+
+def prepare_layout_dispatch(shape: MoeShape, dtype: str, x: torch.Tensor, topk_idx: torch.Tensor,
+                            topk_w: torch.Tensor, lay: Dict[str, torch.Tensor], d: Dict[str, torch.Tensor]) -> Prepared:
+    """run_layout_dispatch with its arguments checked once."""
+    return moe_layout_dispatch(shape, dtype, x, topk_idx, topk_w, lay["tokens_per_rank"], lay["tokens_per_expert"],
+                               lay["is_token_in_rank"], lay["workspace"], d["recv_x"], d["recv_scales"],
+                               d["recv_src_idx"], d["recv_topk_idx"], d["recv_topk_w"], d["rank_offsets"],
+                               d["send_row"], d["num_recv"], prepare=True)
+
+
+def prepare_combine(shape: MoeShape, y: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                    send_row: torch.Tensor, out: torch.Tensor) -> Prepared:
+    """moe_combine with its arguments checked once."""
+    return moe_combine(shape, y, topk_idx, topk_w, send_row, out, prepare=True)
 
 
 def alloc_dispatch_ll(shape: MoeShape, dtype: str, device="cuda", capacity: Optional[int] = None

@@ -147,39 +147,66 @@ def _check(fn: str, code: int) -> None:
         raise MoeError(fn, code)
 
 
+class Prepared:
+    """One library call with its arguments checked and converted once: calling it launches the
+    work on the given stream (default: torch's current stream).  It keeps the tensors it was
+    prepared with alive; they must not be reallocated while it is in use.  For buffers allocated
+    once and reused, as the exchange's are, this takes the per-call argument checks of the Python
+    wrapper off the launch path (the library still checks every call on the host)."""
+
+    __slots__ = ("name", "fn", "args", "keep")
+
+    def __init__(self, name: str, fn, args, keep):
+        self.name, self.fn, self.keep = name, fn, keep
+        self.args = tuple(a if a is None or not isinstance(a, int) else t(a) for a, t in zip(args, fn.argtypes))
+
+    def __call__(self, stream=None) -> None:
+        code = self.fn(*self.args, _stream(stream))
+        if code != MOE_OK:
+            raise MoeError(self.name, code)
+
+
+def _launch(name: str, args, stream, prepare: bool, scope: dict):
+    """Calls library function `name` with `args` and the stream, or returns it as a Prepared call
+    (keeping the tensors among the caller's arguments, `scope`, alive)."""
+    fn = getattr(lib, name)
+    if prepare:
+        return Prepared(name, fn, args, tuple(v for v in scope.values() if isinstance(v, torch.Tensor)))
+    _check(name, fn(*args, _stream(stream)))
+    return None
+
+
 def moe_get_dispatch_layout(shape: MoeShape, topk_idx, tokens_per_rank, tokens_per_expert, is_token_in_rank,
-                            workspace, stream=None) -> None:
+                            workspace, stream=None, prepare: bool = False):
     T, k, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
-    code = lib.moe_get_dispatch_layout(
+    return _launch("moe_get_dispatch_layout", (
         ctypes.byref(shape.c()), _ptr(topk_idx, "topk_idx", torch.int32, T * k),
         _ptr(tokens_per_rank, "tokens_per_rank", torch.int32, R),
         _ptr(tokens_per_expert, "tokens_per_expert", torch.int32, E),
         _ptr(is_token_in_rank, "is_token_in_rank", torch.uint8, T * R),
-        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
-    _check("moe_get_dispatch_layout", code)
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel()), stream, prepare, locals())
 
 
 def moe_route_layout(shape: MoeShape, logits, topk_idx, topk_w, tokens_per_rank, tokens_per_expert,
                      is_token_in_rank, workspace, gate: str = "softmax", num_groups: int = 1, topk_groups: int = 1,
-                     stream=None) -> None:
+                     stream=None, prepare: bool = False):
     T, k, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
     router = MoeRouterC(GATES[gate], int(num_groups), int(topk_groups))
-    code = lib.moe_route_layout(
+    return _launch("moe_route_layout", (
         ctypes.byref(shape.c()), ctypes.byref(router), _ptr(logits, "logits", torch.float32, T * E),
         _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
         _ptr(tokens_per_rank, "tokens_per_rank", torch.int32, R),
         _ptr(tokens_per_expert, "tokens_per_expert", torch.int32, E),
         _ptr(is_token_in_rank, "is_token_in_rank", torch.uint8, T * R),
-        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
-    _check("moe_route_layout", code)
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel()), stream, prepare, locals())
 
 
 def moe_dispatch(shape: MoeShape, dtype: str, x, topk_idx, topk_w, workspace, recv_x, recv_scales, recv_src_idx,
-                 recv_topk_idx, recv_topk_w, rank_offsets, send_row, num_recv, stream=None) -> None:
+                 recv_topk_idx, recv_topk_w, rank_offsets, send_row, num_recv, stream=None, prepare: bool = False):
     T, H, k, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
     fp8 = DTYPES[dtype] == MOE_FP8_E4M3
     cap = recv_src_idx.numel()
-    code = lib.moe_dispatch(
+    return _launch("moe_dispatch", (
         ctypes.byref(shape.c()), DTYPES[dtype], _ptr(x, "x", torch.bfloat16, T * H),
         _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), cap,
@@ -189,18 +216,16 @@ def moe_dispatch(shape: MoeShape, dtype: str, x, topk_idx, topk_w, workspace, re
         _ptr(recv_topk_idx, "recv_topk_idx", torch.int32, cap * k),
         _ptr(recv_topk_w, "recv_topk_w", torch.float32, cap * k),
         _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),
-        _ptr(send_row, "send_row", torch.int32, T * R), _ptr(num_recv, "num_recv", torch.int32, 1),
-        _stream(stream))
-    _check("moe_dispatch", code)
+        _ptr(send_row, "send_row", torch.int32, T * R), _ptr(num_recv, "num_recv", torch.int32, 1)), stream, prepare, locals())
 
 
 def moe_layout_dispatch(shape: MoeShape, dtype: str, x, topk_idx, topk_w, tokens_per_rank, tokens_per_expert,
                         is_token_in_rank, workspace, recv_x, recv_scales, recv_src_idx, recv_topk_idx, recv_topk_w,
-                        rank_offsets, send_row, num_recv, stream=None) -> None:
+                        rank_offsets, send_row, num_recv, stream=None, prepare: bool = False):
     T, H, k, E, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts, shape.num_ranks
     fp8 = DTYPES[dtype] == MOE_FP8_E4M3
     cap = recv_src_idx.numel()
-    code = lib.moe_layout_dispatch(
+    return _launch("moe_layout_dispatch", (
         ctypes.byref(shape.c()), DTYPES[dtype], _ptr(x, "x", torch.bfloat16, T * H),
         _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
         _ptr(tokens_per_rank, "tokens_per_rank", torch.int32, R),
@@ -213,81 +238,71 @@ def moe_layout_dispatch(shape: MoeShape, dtype: str, x, topk_idx, topk_w, tokens
         _ptr(recv_topk_idx, "recv_topk_idx", torch.int32, cap * k),
         _ptr(recv_topk_w, "recv_topk_w", torch.float32, cap * k),
         _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),
-        _ptr(send_row, "send_row", torch.int32, T * R), _ptr(num_recv, "num_recv", torch.int32, 1),
-        _stream(stream))
-    _check("moe_layout_dispatch", code)
+        _ptr(send_row, "send_row", torch.int32, T * R), _ptr(num_recv, "num_recv", torch.int32, 1)), stream, prepare, locals())
 
 
-def moe_combine(shape: MoeShape, y, topk_idx, topk_w, send_row, out, stream=None, num_y_rows=None) -> None:
+def moe_combine(shape: MoeShape, y, topk_idx, topk_w, send_row, out, stream=None, prepare: bool = False, num_y_rows=None):
     T, H, k, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
     rows = y.shape[0] if num_y_rows is None else int(num_y_rows)
-    code = lib.moe_combine(
+    return _launch("moe_combine", (
         ctypes.byref(shape.c()), _ptr(y, "y", torch.bfloat16, rows * H), rows,
         _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
-        _ptr(send_row, "send_row", torch.int32, T * R), _ptr(out, "out", torch.bfloat16, T * H), _stream(stream))
-    _check("moe_combine", code)
+        _ptr(send_row, "send_row", torch.int32, T * R), _ptr(out, "out", torch.bfloat16, T * H)), stream, prepare, locals())
 
 
 def moe_dispatch_ll(shape: MoeShape, dtype: str, x, topk_idx, workspace, recv_x, recv_scales, recv_src_idx,
-                    recv_count, slot_pos, stream=None) -> None:
+                    recv_count, slot_pos, stream=None, prepare: bool = False):
     T, H, k, E = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts
     fp8 = DTYPES[dtype] == MOE_FP8_E4M3
     cap = recv_src_idx.shape[1] if recv_src_idx.dim() == 2 else recv_src_idx.numel() // max(E, 1)
-    code = lib.moe_dispatch_ll(
+    return _launch("moe_dispatch_ll", (
         ctypes.byref(shape.c()), DTYPES[dtype], _ptr(x, "x", torch.bfloat16, T * H),
         _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(workspace, "workspace", torch.uint8),
         workspace.numel(), cap, _ptr(recv_x, "recv_x", torch.uint8 if fp8 else torch.bfloat16, E * cap * H),
         _ptr(recv_scales, "recv_scales", torch.float32, E * cap * (H // 128)) if fp8 else None,
         _ptr(recv_src_idx, "recv_src_idx", torch.int32, E * cap), _ptr(recv_count, "recv_count", torch.int32, E),
-        _ptr(slot_pos, "slot_pos", torch.int32, T * k), _stream(stream))
-    _check("moe_dispatch_ll", code)
+        _ptr(slot_pos, "slot_pos", torch.int32, T * k)), stream, prepare, locals())
 
 
-def moe_combine_ll(shape: MoeShape, y, topk_idx, topk_w, slot_pos, out, stream=None) -> None:
+def moe_combine_ll(shape: MoeShape, y, topk_idx, topk_w, slot_pos, out, stream=None, prepare: bool = False):
     T, H, k, E = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts
     cap = y.shape[1]
-    code = lib.moe_combine_ll(
+    return _launch("moe_combine_ll", (
         ctypes.byref(shape.c()), _ptr(y, "y", torch.bfloat16, E * cap * H), cap,
         _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
-        _ptr(slot_pos, "slot_pos", torch.int32, T * k), _ptr(out, "out", torch.bfloat16, T * H), _stream(stream))
-    _check("moe_combine_ll", code)
+        _ptr(slot_pos, "slot_pos", torch.int32, T * k), _ptr(out, "out", torch.bfloat16, T * H)), stream, prepare, locals())
 
 
-def moe_encode_e4m3(values, codes, stream=None) -> None:
+def moe_encode_e4m3(values, codes, stream=None, prepare: bool = False):
     """codes (uint8) = E4M3 round-to-nearest-even codes of values (float32), as the FP8 dispatch
     rounds x / s; defined for finite |values| < 464."""
     n = values.numel()
     if codes.numel() != n:
         raise ValueError(f"codes: {codes.numel()} elements for {n} values")
-    code = lib.moe_encode_e4m3(_ptr(values, "values", torch.float32, n), _ptr(codes, "codes", torch.uint8, n), n,
-                               _stream(stream))
-    _check("moe_encode_e4m3", code)
+    return _launch("moe_encode_e4m3", (_ptr(values, "values", torch.float32, n), _ptr(codes, "codes", torch.uint8, n),
+                                       n), stream, prepare, locals())
 
 
 def moe_combine_backward(shape: MoeShape, grad_out, y, topk_idx, topk_w, send_row, grad_y, grad_topk_w,
-                         stream=None, num_y_rows=None) -> None:
+                         stream=None, prepare: bool = False, num_y_rows=None):
     T, H, k, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
     rows = y.shape[0] if num_y_rows is None else int(num_y_rows)
-    code = lib.moe_combine_backward(
+    return _launch("moe_combine_backward", (
         ctypes.byref(shape.c()), _ptr(grad_out, "grad_out", torch.bfloat16, T * H),
         _ptr(y, "y", torch.bfloat16, rows * H), rows, _ptr(topk_idx, "topk_idx", torch.int32, T * k),
         _ptr(topk_w, "topk_w", torch.float32, T * k), _ptr(send_row, "send_row", torch.int32, T * R),
-        _ptr(grad_y, "grad_y", torch.bfloat16, rows * H), _ptr(grad_topk_w, "grad_topk_w", torch.float32, T * k),
-        _stream(stream))
-    _check("moe_combine_backward", code)
+        _ptr(grad_y, "grad_y", torch.bfloat16, rows * H), _ptr(grad_topk_w, "grad_topk_w", torch.float32, T * k)), stream, prepare, locals())
 
 
 def moe_dispatch_backward(shape: MoeShape, grad_recv_x, topk_idx, send_row, grad_x, grad_recv_topk_w=None,
-                          grad_topk_w=None, stream=None, num_recv_rows=None) -> None:
+                          grad_topk_w=None, stream=None, prepare: bool = False, num_recv_rows=None):
     T, H, k, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
     rows = grad_recv_x.shape[0] if num_recv_rows is None else int(num_recv_rows)
-    code = lib.moe_dispatch_backward(
+    return _launch("moe_dispatch_backward", (
         ctypes.byref(shape.c()), _ptr(grad_recv_x, "grad_recv_x", torch.bfloat16, rows * H), rows,
         _ptr(grad_recv_topk_w, "grad_recv_topk_w", torch.float32, rows * k),
         _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(send_row, "send_row", torch.int32, T * R),
-        _ptr(grad_x, "grad_x", torch.bfloat16, T * H), _ptr(grad_topk_w, "grad_topk_w", torch.float32, T * k),
-        _stream(stream))
-    _check("moe_dispatch_backward", code)
+        _ptr(grad_x, "grad_x", torch.bfloat16, T * H), _ptr(grad_topk_w, "grad_topk_w", torch.float32, T * k)), stream, prepare, locals())
 
 
 def stream_create_cu_range(first_cu: int, num_cus: int) -> int:
