@@ -189,3 +189,16 @@ def test_layout_dispatch_rejections():
     assert call(x=A + 2) == INVALID  # misaligned x
     assert call(dtype=1, scales=None) == INVALID  # FP8 needs scales
     assert fn(None, 0, A, A, A, A, A, A, A, 1 << 30, cap, A, A, A, A, A, A, A, A, None) == INVALID
+
+
+def test_prepared_call_checks_its_tensors_once_at_prepare_time():
+    """prepare=True runs the wrapper's tensor checks up front (CPU tensors are refused) and
+    converts the remaining integer arguments to the declared ctypes types."""
+    import torch
+    sh = L.MoeShape(8, 256, 4, 16, 4)
+    with pytest.raises(ValueError):
+        L.moe_combine(sh, torch.zeros(8, 256, dtype=torch.bfloat16), torch.zeros(8, 4, dtype=torch.int32),
+                      torch.zeros(8, 4), torch.zeros(8, 4, dtype=torch.int32),
+                      torch.zeros(8, 256, dtype=torch.bfloat16), prepare=True)
+    p = L.Prepared("moe_encode_e4m3", L.lib.moe_encode_e4m3, (A, A, 0), ())
+    assert isinstance(p.args[2], ctypes.c_int64) and p.args[0].value == A

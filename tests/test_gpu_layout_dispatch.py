@@ -128,3 +128,43 @@ def test_layout_dispatch_edges(case):
 def test_empty_batch():
     x = np.zeros((0, 256), np.uint16)
     run_fused_case(x, np.zeros((0, 4), np.int32), np.zeros((0, 4), np.float32), 16, 4, "bf16")
+
+
+def test_prepared_calls_match_direct_calls():
+    """prepare_* calls (arguments checked once) give the direct calls' bytes, called twice."""
+    import combine_get_dispatch_07_amd as moe
+    from tests.gpu_harness import to_dev_bf16
+
+    cfg = W.CONFIG_BY_NAME["decode"]
+    print("[case] prepared calls, decode", flush=True)
+    shape = moe.MoeShape(cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks)
+    d = W.make_inputs(cfg)
+    x = to_dev_bf16(d["x"])
+    idx = torch.from_numpy(d["topk_idx"]).cuda()
+    w = torch.from_numpy(d["topk_w"]).cuda()
+    y = to_dev_bf16(W.draw_expert_outputs(np.random.default_rng(2), moe.max_recv_rows(shape), cfg.hidden))
+    cap = moe.max_recv_rows(shape)
+
+    lay_a, d_a = _bufs(moe, shape, "fp8", cap)
+    out_a = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    moe.run_layout(shape, idx, lay_a)
+    moe.run_dispatch(shape, "fp8", x, idx, w, lay_a, d_a)
+    moe.moe_combine(shape, y, idx, w, d_a["send_row"], out_a)
+
+    lay_b, d_b = _bufs(moe, shape, "fp8", cap)
+    out_b = torch.empty_like(out_a)
+    calls = [moe.prepare_layout(shape, idx, lay_b), moe.prepare_dispatch(shape, "fp8", x, idx, w, lay_b, d_b),
+             moe.prepare_combine(shape, y, idx, w, d_b["send_row"], out_b)]
+    for _ in range(2):
+        for c in calls:
+            c()
+    lay_c, d_c = _bufs(moe, shape, "fp8", cap)
+    one = moe.prepare_layout_dispatch(shape, "fp8", x, idx, w, lay_c, d_c)
+    one()
+    one()
+    torch.cuda.synchronize()
+    a, b, c = _host(lay_a, d_a), _host(lay_b, d_b), _host(lay_c, d_c)
+    for key in a:
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+        assert np.array_equal(a[key].view(np.uint8), c[key].view(np.uint8)), key
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
