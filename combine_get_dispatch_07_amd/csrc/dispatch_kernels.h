@@ -90,6 +90,47 @@ __device__ __forceinline__ float block_amax(u32x4 v) {
   return __uint_as_float(lanes_max<16>(m) << 16);
 }
 
+// FP8 codes and block scales of a wave's slice, this lane's U 16-byte pieces:
+// one scale per 128 channels (16 lanes), s = fl32(max(amax, 1e-4) / 448).
+template <int U>
+__device__ __forceinline__ void quantize_slice(const u32x4 (&v)[U], u32x2 (&q)[U], float (&sc)[U]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    sc[u] = fmaxf(block_amax(v[u]), kAmaxFloor) / kE4m3Max;
+    q[u] = quantize8(v[u], sc[u]);
+  }
+}
+
+// Writes this lane's pieces of a slice (piece u covers 16-byte column c0 + 64u
+// of the row) to receive row `row`: the bf16 bits, or the E4M3 codes and, from
+// the first lane of each 16, the block scale.  Nontemporal stores: the receive
+// rows are not read again by the dispatch.
+template <int U, bool kFp8>
+__device__ __forceinline__ void store_slice(void* recv_x, float* recv_scales, size_t row, int H, int H8, int c0,
+                                            int lane, const u32x4 (&v)[U], const u32x2 (&q)[U],
+                                            const float (&sc)[U]) {
+  if constexpr (kFp8) {
+    u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint8_t*>(recv_x) + row * H);
+    float* sdst = recv_scales + row * (H / kFp8Block);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave;
+      if (c < H8) {
+        __builtin_nontemporal_store(q[u], dst + c);
+        if ((lane & 15) == 0) sdst[c >> 4] = sc[u];
+      }
+    }
+  } else {
+    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(recv_x) + row * H);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave;
+      if (c < H8) __builtin_nontemporal_store(v[u], dst + c);
+    }
+  }
+}
+
 // Every load is issued unconditionally from a clamped, always valid address
 // and masked afterwards: a load under a lane-dependent branch makes the
 // compiler wait for it before the branch joins, which would serialise the
@@ -128,14 +169,7 @@ __device__ __forceinline__ void dispatch_item(const DispatchArgs& a, int item, i
 
   u32x2 q[U];
   float sc[U];
-  if constexpr (kFp8) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float amax = block_amax(v[u]);
-      sc[u] = fmaxf(amax, kAmaxFloor) / kE4m3Max;
-      q[u] = quantize8(v[u], sc[u]);
-    }
-  }
+  if constexpr (kFp8) quantize_slice<U>(v, q, sc);
 
   // Slot metadata: lane j < k holds slot j of this token.
   const bool meta = s == 0;
@@ -153,25 +187,7 @@ __device__ __forceinline__ void dispatch_item(const DispatchArgs& a, int item, i
     if ((unsigned)row >= (unsigned)a.capacity) continue;  // only a plan from another layout gets here
     my_row = lane == r ? row : my_row;
 
-    if constexpr (kFp8) {
-      u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.recv_x) + (size_t)row * a.H);
-      float* sdst = a.recv_scales + (size_t)row * (a.H / kFp8Block);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * kWave;
-        if (c < a.H8) {
-          __builtin_nontemporal_store(q[u], dst + c);
-          if ((lane & 15) == 0) sdst[c >> 4] = sc[u];
-        }
-      }
-    } else {
-      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.recv_x) + (size_t)row * a.H);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * kWave;
-        if (c < a.H8) __builtin_nontemporal_store(v[u], dst + c);
-      }
-    }
+    store_slice<U, kFp8>(a.recv_x, a.recv_scales, (size_t)row, a.H, a.H8, c0, lane, v, q, sc);
 
     if (meta) {
       if (lane == 0) a.recv_src_idx[row] = t;

@@ -151,13 +151,7 @@ __global__ __launch_bounds__(kDispatchBlock) void ll_dispatch_kernel(LlDispatchA
     if (c0 + u * kWave >= a.H8) v[u] = u32x4{0u, 0u, 0u, 0u};
   u32x2 q[U];
   float sc[U];
-  if constexpr (kFp8) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      sc[u] = fmaxf(block_amax(v[u]), kAmaxFloor) / kE4m3Max;
-      q[u] = quantize8(v[u], sc[u]);
-    }
-  }
+  if constexpr (kFp8) quantize_slice<U>(v, q, sc);
 
   if (s == 0 && lane < a.k) a.slot_pos[(size_t)t * a.k + lane] = pos;
   uint64_t todo = __ballot(first);
@@ -168,25 +162,7 @@ __global__ __launch_bounds__(kDispatchBlock) void ll_dispatch_kernel(LlDispatchA
     const int pj = __builtin_amdgcn_readlane(pos, j);
     const size_t row = (size_t)ej * a.cap + pj;
     if (s == 0 && lane == 0) a.recv_src_idx[row] = t;
-    if constexpr (kFp8) {
-      u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.recv_x) + row * a.H);
-      float* sdst = a.recv_scales + row * (a.H / kFp8Block);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * kWave;
-        if (c < a.H8) {
-          __builtin_nontemporal_store(q[u], dst + c);
-          if ((lane & 15) == 0) sdst[c >> 4] = sc[u];
-        }
-      }
-    } else {
-      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.recv_x) + row * a.H);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * kWave;
-        if (c < a.H8) __builtin_nontemporal_store(v[u], dst + c);
-      }
-    }
+    store_slice<U, kFp8>(a.recv_x, a.recv_scales, (size_t)row, a.H, a.H8, c0, lane, v, q, sc);
   }
 }
 
@@ -291,13 +267,7 @@ __global__ __launch_bounds__(kLlSmallMaxWaves * kWave) void ll_dispatch_small_ke
     if (c0 + uu * kWave >= a.H8) v[uu] = u32x4{0u, 0u, 0u, 0u};
   u32x2 q[U];
   float sc[U];
-  if constexpr (kFp8) {
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      sc[uu] = fmaxf(block_amax(v[uu]), kAmaxFloor) / kE4m3Max;
-      q[uu] = quantize8(v[uu], sc[uu]);
-    }
-  }
+  if constexpr (kFp8) quantize_slice<U>(v, q, sc);
   __syncthreads();
 
   int pos = valid ? cnt[lane] : -1;
@@ -314,25 +284,7 @@ __global__ __launch_bounds__(kLlSmallMaxWaves * kWave) void ll_dispatch_small_ke
     const int pj = __builtin_amdgcn_readlane(pos, j);
     const size_t row = (size_t)ej * a.cap + pj;
     if (wave == 0 && lane == 0) a.recv_src_idx[row] = t;
-    if constexpr (kFp8) {
-      u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.recv_x) + row * a.H);
-      float* sdst = a.recv_scales + row * (a.H / kFp8Block);
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        const int c = c0 + uu * kWave;
-        if (c < a.H8) {
-          __builtin_nontemporal_store(q[uu], dst + c);
-          if ((lane & 15) == 0) sdst[c >> 4] = sc[uu];
-        }
-      }
-    } else {
-      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.recv_x) + row * a.H);
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        const int c = c0 + uu * kWave;
-        if (c < a.H8) __builtin_nontemporal_store(v[uu], dst + c);
-      }
-    }
+    store_slice<U, kFp8>(a.recv_x, a.recv_scales, (size_t)row, a.H, a.H8, c0, lane, v, q, sc);
   }
 }
 

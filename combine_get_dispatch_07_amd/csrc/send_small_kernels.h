@@ -123,13 +123,7 @@ __global__ __launch_bounds__(kSendSmallMaxWaves * kWave) void send_small_kernel(
     if (c0 + uu * kWave >= a.H8) v[uu] = u32x4{0u, 0u, 0u, 0u};
   u32x2 q[U];
   float sc[U];
-  if constexpr (kFp8) {
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      sc[uu] = fmaxf(block_amax(v[uu]), kAmaxFloor) / kE4m3Max;
-      q[uu] = quantize8(v[uu], sc[uu]);
-    }
-  }
+  if constexpr (kFp8) quantize_slice<U>(v, q, sc);
   __syncthreads();
 
   // lane r < R: the segment offset of rank r (exclusive scan of the totals) plus
@@ -145,25 +139,7 @@ __global__ __launch_bounds__(kSendSmallMaxWaves * kWave) void send_small_kernel(
     const int row = __builtin_amdgcn_readlane(rank_row, r);
     if ((unsigned)row >= (unsigned)a.capacity) continue;  // unreachable: capacity is checked on the host
     my_row = lane == r ? row : my_row;
-    if constexpr (kFp8) {
-      u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.recv_x) + (size_t)row * a.H);
-      float* sdst = a.recv_scales + (size_t)row * (a.H / kFp8Block);
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        const int c = c0 + uu * kWave;
-        if (c < a.H8) {
-          __builtin_nontemporal_store(q[uu], dst + c);
-          if ((lane & 15) == 0) sdst[c >> 4] = sc[uu];
-        }
-      }
-    } else {
-      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.recv_x) + (size_t)row * a.H);
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        const int c = c0 + uu * kWave;
-        if (c < a.H8) __builtin_nontemporal_store(v[uu], dst + c);
-      }
-    }
+    store_slice<U, kFp8>(a.recv_x, a.recv_scales, (size_t)row, a.H, a.H8, c0, lane, v, q, sc);
     if (meta) {
       if (lane == 0) a.recv_src_idx[row] = t;
       if (lane < a.k) {
