@@ -93,3 +93,24 @@ def test_backward_prefill_workload():
 ])
 def test_backward_edges(case):
     run_backward_case(*case)
+
+
+def _bwd_random_shapes(n: int, seed: int = 0xB4C):
+    """Seeded shapes inside the limits: R | E, k <= min(E, 32), H % 8 == 0."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([1, 2, 3, 4, 6, 8, 16, 32, 64]))
+        L = int(rng.integers(1, max(2, 256 // R) + 1))
+        E = R * L
+        k = int(rng.integers(1, min(E, 32) + 1))
+        H = 8 * int(rng.integers(1, 161))
+        T = int(rng.integers(1, 1500))
+        inv = float(rng.choice([0.0, 0.1, 0.4]))
+        out.append((T, H, E, k, R, 300 + i, inv))
+    return out
+
+
+@pytest.mark.parametrize("case", _bwd_random_shapes(8), ids=lambda c: "T{}_H{}_E{}_k{}_R{}".format(*c[:5]))
+def test_backward_random_shapes(case):
+    run_backward_case(*case)

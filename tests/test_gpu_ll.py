@@ -79,6 +79,41 @@ def test_ll_decode_workload():
     run_ll_case(d["x"], d["topk_idx"], d["topk_w"], cfg.num_experts, cfg.num_tokens, "fp8", seed=1)
 
 
+def _ll_random_shapes(n: int, seed: int = 0x11ED):
+    """Seeded shapes for the per-expert layout, kept to E * cap * H <= 2^25 elements per buffer."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        E = int(rng.integers(1, 513))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        dtype = "fp8" if rng.random() < 0.5 else "bf16"
+        H = 128 * int(rng.integers(1, 9)) if dtype == "fp8" else 8 * int(rng.integers(1, 129))
+        T = int(rng.integers(1, 1300))
+        extra = int(rng.integers(0, 4))
+        if E * (T + extra) * H > 1 << 25:
+            continue
+        inv = float(rng.choice([0.0, 0.1, 0.4]))
+        out.append((f"rand{len(out)}_T{T}_H{H}_E{E}_k{k}_{dtype}", 200 + len(out), T, H, E, k, dtype, inv, extra))
+    return out
+
+
+LL_RANDOM_SHAPES = _ll_random_shapes(8)
+
+
+@pytest.mark.parametrize("case", LL_RANDOM_SHAPES, ids=lambda c: c[0])
+def test_ll_random_shapes(case):
+    _ll_edge(case)
+
+
+def _ll_edge(case):
+    name, seed, T, H, E, k, dtype, inv, extra = case
+    d = W.random_case(seed, T, H, E, k, 1, invalid_frac=inv)
+    idx = d["topk_idx"].copy()
+    if T > 3:
+        idx[2, :2] = max(int(idx[2, 0]), 0)  # one token names an expert twice
+    run_ll_case(d["x"], idx, d["topk_w"], E, T + extra, dtype, seed=seed)
+
+
 @pytest.mark.parametrize("case", [
     # name, seed, T, H, E, k, dtype, invalid_frac, capacity extra
     ("small_bf16", 1, 37, 256, 16, 4, "bf16", 0.2, 5),
@@ -91,12 +126,7 @@ def test_ll_decode_workload():
     ("small_last_batch", 8, 129, 256, 64, 8, "fp8", 0.0, 1),        # one token in the last 64-token batch
 ])
 def test_ll_edges(case):
-    name, seed, T, H, E, k, dtype, inv, extra = case
-    d = W.random_case(seed, T, H, E, k, 1, invalid_frac=inv)
-    idx = d["topk_idx"].copy()
-    if T > 3:
-        idx[2, :2] = max(int(idx[2, 0]), 0)  # one token names an expert twice
-    run_ll_case(d["x"], idx, d["topk_w"], E, T + extra, dtype, seed=seed)
+    _ll_edge(case)
 
 
 def test_ll_empty_and_capacity_error():

@@ -155,10 +155,33 @@ EDGE = [
     ("wide_hidden_fp8", 13, 300, 16384, 64, 8, 8, "fp8", 0.0),     # 2048 16-byte pieces per row
     ("wide_hidden_bf16", 14, 300, 16384, 64, 8, 8, "bf16", 0.05),
     ("many_chunks", 15, 70000, 64, 64, 4, 8, "bf16", 0.05),      # 1094 chunks: multi-pass chunk scans
+    ("one_expert_per_rank_k_eq_E", 16, 513, 256, 8, 8, 8, "bf16", 0.0),  # L = 1, every token to every rank
+    ("min_hidden_bf16", 17, 1500, 8, 32, 4, 8, "bf16", 0.05),   # one 16-byte piece per row
+    ("min_hidden_fp8", 18, 1500, 128, 32, 4, 8, "fp8", 0.05),   # one scale block per row
 ]
 
 
-@pytest.mark.parametrize("case", EDGE, ids=lambda c: c[0])
+def _random_shapes(n: int, seed: int = 0xED6E):
+    """Seeded shapes inside the library's limits: R | E, k <= E, H % 8 == 0 (H % 128 for FP8)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 32, 64]))
+        L = int(rng.integers(1, max(2, 512 // R) + 1))
+        E = R * L
+        k = int(rng.integers(1, min(E, 32) + 1))
+        dtype = "fp8" if rng.random() < 0.5 else "bf16"
+        H = 128 * int(rng.integers(1, 13)) if dtype == "fp8" else 8 * int(rng.integers(1, 161))
+        T = int(rng.integers(0, 2600))
+        inv = float(rng.choice([0.0, 0.0, 0.1, 0.5]))
+        out.append((f"rand{i}_T{T}_H{H}_E{E}_k{k}_R{R}_{dtype}", 100 + i, T, H, E, k, R, dtype, inv))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(16)
+
+
+@pytest.mark.parametrize("case", EDGE + RANDOM_SHAPES, ids=lambda c: c[0])
 def test_edge_parity(case):
     name, seed, T, Hd, E, k, R, dtype, inv = case
     _print_case("edge", name=name, T=T, H=Hd, E=E, k=k, R=R, dtype=dtype)
