@@ -40,3 +40,16 @@ def test_algorithmic_bytes_fp8_scales():
     b = bench.algorithmic_bytes(cfg, n)
     # FP8 rows: H bytes of codes plus one fp32 scale per 128 channels
     assert b["dispatch"] == T * H * 2 + T * k * 8 + T * R + n * (H + 4 * H // 128 + 4 + 8 * k) + T * R * 4
+
+
+def test_rotation_keeps_source_rows_out_of_the_last_level_cache():
+    llc = 256 << 20
+    for cfg in W.CONFIGS:
+        x_bytes = cfg.num_tokens * cfg.hidden * 2
+        n = bench.rotation_sets(10 << 20, x_bytes)
+        assert 3 <= n <= bench.MAX_SETS
+        if n < bench.MAX_SETS:  # the other sets' source rows cover twice the cache
+            assert (n - 1) * x_bytes >= 2 * llc, cfg.name
+    assert bench.rotation_sets(900 << 20, 4096 * 7168 * 2) == 11  # prefill: 58.7 MB of rows per set
+    assert bench.rotation_sets(3 << 30, 16384 * 7168 * 2) == 4    # 16384 tokens: 235 MB per set
+    assert bench.rotation_sets(20 << 20, 128 * 7168 * 2) == bench.MAX_SETS  # decode
