@@ -178,6 +178,10 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(moe::u32x4* p, size_t n1
     p[i] = moe::u32x4{0u, 0u, 0u, 0u};
 }
 
+__global__ __launch_bounds__(256) void zero_fill_f32_kernel(float* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.0f;
+}
+
 // Combine over T tokens: one wave per (token, 512-channel slice) item, on a
 // persistent grid.  With no rows of y every slot is skipped and out is +0.
 template <int kMode>
@@ -771,6 +775,12 @@ moe_status moe_combine_backward(const moe_shape* shape, const void* grad_out, co
       !aligned(topk_w, 4) || !aligned(send_row, 4) || !aligned(grad_topk_w, 4))
     return MOE_ERR_INVALID_ARG;
   if (s.num_tokens == 0) return MOE_OK;
+  if (num_y_rows == 0) {  // no expert rows: grad_y has no row to write and every weight gradient is +0
+    const size_t n = (size_t)s.num_tokens * s.num_topk;
+    const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_fill_f32_kernel, dim3(blocks), dim3(256), 0, stream, grad_topk_w, n);
+    return last_launch_status();
+  }
 
   moe::CombineBwdArgs a{};
   a.g = static_cast<const uint16_t*>(grad_out);
@@ -790,7 +800,7 @@ moe_status moe_combine_backward(const moe_shape* shape, const void* grad_out, co
   a.num_y_rows = num_y_rows;
   const int slices = (a.H8 + moe::kWave - 1) / moe::kWave;
   const dim3 grid(s.num_tokens), block(std::min(slices, MOE_BWD_WAVES) * moe::kWave);
-  if (s.num_topk <= 8)
+  if (s.num_topk <= moe::kNarrowTopk)
     hipLaunchKernelGGL(moe::combine_backward_kernel, grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL(moe::combine_backward_wide_kernel, grid, block, 0, stream, a);

@@ -299,6 +299,9 @@ moe_status moe_combine_ll(const moe_shape* shape, const void* y, int32_t expert_
  *                                           refers to are not written
  *   grad_topk_w  out float[T, k]            <grad_out[t], y[row(t, j)]> summed in fp32 in a
  *                                           fixed order (deterministic); 0 for invalid slots
+ *                                           and for slots whose row is not below num_y_rows
+ * With num_y_rows == 0, y and grad_y may be NULL: nothing is written to grad_y and every
+ * grad_topk_w is +0.
  */
 moe_status moe_combine_backward(const moe_shape* shape, const void* grad_out, const void* y, int32_t num_y_rows,
                                 const int32_t* topk_idx, const float* topk_w, const int32_t* send_row,

@@ -90,6 +90,12 @@ def test_backward_prefill_workload():
     (300, 256, 128, 16, 32, 7, 0.1),   # min(k, R) = 16: compacted rows in two batches
     (100, 128, 64, 32, 64, 8, 0.0),    # k = 32: widest combine backward, four batches
     (150, 136, 64, 32, 4, 9, 0.1),     # k = 32 on 4 ranks: eight slots share each y row, ragged hidden
+    # larger batches, k <= 8
+    (1024, 512, 64, 6, 16, 10, 0.1),   # exactly one token per wave on the full chip
+    (2500, 136, 64, 8, 8, 11, 0.2),    # ragged hidden, tokens not a multiple of the waves
+    (1100, 64, 16, 1, 4, 12, 0.0),     # one slice per token (8 of 64 lanes in range), k = 1
+    (3001, 256, 256, 8, 64, 13, 0.6),  # R = 64, mostly invalid ids
+    (4099, 1024, 32, 4, 4, 14, 0.0),   # two slices, duplicate ranks within a token
 ])
 def test_backward_edges(case):
     run_backward_case(*case)
@@ -114,3 +120,22 @@ def _bwd_random_shapes(n: int, seed: int = 0xB4C):
 @pytest.mark.parametrize("case", _bwd_random_shapes(8), ids=lambda c: "T{}_H{}_E{}_k{}_R{}".format(*c[:5]))
 def test_backward_random_shapes(case):
     run_backward_case(*case)
+
+
+def test_combine_backward_without_expert_rows():
+    """num_y_rows = 0 (y and grad_y empty): nothing is written to grad_y and every weight gradient is +0."""
+    import combine_get_dispatch_07_amd as moe
+    T, H, E, k, R = 300, 256, 16, 4, 4
+    print(f"[case] backward without expert rows T={T} H={H}", flush=True)
+    d = W.random_case(21, T, H, E, k, R)
+    _, _, mask = O.get_dispatch_layout(d["topk_idx"], E, R)
+    _, send_row, _ = O.assign_slots(mask)
+    g = W.draw_expert_outputs(np.random.default_rng(21), T, H)
+    empty = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    gw_d = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    shape = moe.MoeShape(T, H, k, E, R)
+    moe.moe_combine_backward(shape, _dev(g), empty, _dev(d["topk_idx"]), _dev(d["topk_w"]), _dev(send_row), empty,
+                             gw_d, num_y_rows=0)
+    torch.cuda.synchronize()
+    gw = gw_d.cpu().numpy()
+    assert (gw.view(np.uint32) == 0).all()
