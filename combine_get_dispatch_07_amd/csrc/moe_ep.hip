@@ -47,7 +47,8 @@ moe_status check_shape(const moe_shape* s) {
   if (T < 0 || H <= 0 || H % 8 != 0 || k < 1 || E < 1 || R < 1) return MOE_ERR_INVALID_ARG;
   if (k > kMaxTopk || R > kMaxRanks || E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (R > E || E % R != 0 || k > E) return MOE_ERR_INVALID_ARG;
-  if (T * k > INT32_MAX || T * R > INT32_MAX || T * std::min(k, R) > INT32_MAX)
+  // T <= 2^30 leaves int headroom for the token-derived launch arithmetic (T + 63, T + 1, ...).
+  if (T > (int64_t)1 << 30 || T * k > INT32_MAX || T * R > INT32_MAX || T * std::min(k, R) > INT32_MAX)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

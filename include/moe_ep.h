@@ -46,7 +46,7 @@
  * - Arguments are checked on the host before anything is enqueued; on any
  *   error nothing is launched and no memory is touched.  A launch failure
  *   reported by the runtime returns MOE_ERR_HIP.
- * - Limits: 0 <= T, 1 <= k <= 32, 1 <= R <= 64, R <= E <= 4096, E % R == 0,
+ * - Limits: 0 <= T <= 2^30, 1 <= k <= 32, 1 <= R <= 64, R <= E <= 4096, E % R == 0,
  *   H > 0 and H % 8 == 0 (H % 128 == 0 for FP8), T*k and T*R below 2^31.
  */
 #ifndef MOE_EP_H_
@@ -71,7 +71,10 @@ typedef struct moe_shape {
 
 typedef enum moe_dtype {
   MOE_BF16 = 0,     /* receive rows are bf16 bit copies of x */
-  MOE_FP8_E4M3 = 1  /* receive rows are OCP E4M3 bytes + fp32 scale per 128 channels */
+  MOE_FP8_E4M3 = 1, /* receive rows are OCP E4M3 bytes + fp32 scale per 128 channels */
+  MOE_DTYPE_MAX_ENUM = 0x7fffffff /* not a dtype: makes the type 32 bits wide and every
+                                     non-negative value a caller passes representable (rejected
+                                     with MOE_ERR_INVALID_ARG unless listed above) */
 } moe_dtype;
 
 typedef enum moe_status {
@@ -79,7 +82,8 @@ typedef enum moe_status {
   MOE_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad shape, workspace too small */
   MOE_ERR_CAPACITY = 2,    /* receive capacity below T * min(k, R) */
   MOE_ERR_UNSUPPORTED = 3, /* shape outside the limits above */
-  MOE_ERR_HIP = 4          /* the HIP runtime reported a launch error */
+  MOE_ERR_HIP = 4,         /* the HIP runtime reported a launch error */
+  MOE_STATUS_MAX_ENUM = 0x7fffffff /* not a status: makes the type 32 bits wide */
 } moe_status;
 
 /* Human-readable name of a status code (static string, never NULL). */

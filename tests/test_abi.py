@@ -75,7 +75,7 @@ def test_sizes():
     (dict(T=-1), INVALID), (dict(H=0), INVALID), (dict(H=12), INVALID), (dict(k=0), INVALID),
     (dict(E=0), INVALID), (dict(R=0), INVALID), (dict(E=16, R=3), INVALID), (dict(E=4, R=8), INVALID),
     (dict(k=5, E=4, R=4), INVALID), (dict(k=33, E=64), UNSUPPORTED), (dict(R=128, E=256), UNSUPPORTED),
-    (dict(E=8192, R=8), UNSUPPORTED),
+    (dict(E=8192, R=8), UNSUPPORTED), (dict(T=(1 << 30) + 1, k=1, E=1, R=1), UNSUPPORTED),
 ])
 def test_shape_errors(kw, code):
     s = shape(**kw)
