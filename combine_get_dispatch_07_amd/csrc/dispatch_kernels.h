@@ -163,11 +163,18 @@ __device__ __forceinline__ void dispatch_item(const DispatchArgs& a, int item, i
   const uint64_t lm_raw = a.token_ranks[min(tt, a.T - 1)];
   const int seg = a.ws_rank_offsets[rl];
   const int cb = a.chunk_base[rl * a.NC + chunk];
-  const int ej_raw = a.topk_idx[(size_t)t * a.k + jl];
-  const float wj_raw = a.topk_w[(size_t)t * a.k + jl];
   u32x4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) v[u] = load_source<kFp8>(xrow + min(c0 + u * kWave, a.H8 - 1));
+  // Only the first slice's wave writes the slot metadata.  bf16 rows are split into many slices,
+  // and loading the slots in that wave alone (a wave-uniform branch) took ~1 us off the prefill
+  // copy; for FP8 every wave loading them measured faster.
+  int ej_raw = -1;
+  float wj_raw = 0.0f;
+  if (kFp8 || s == 0) {
+    ej_raw = a.topk_idx[(size_t)t * a.k + jl];
+    wj_raw = a.topk_w[(size_t)t * a.k + jl];
+  }
 
   const uint64_t lm = tt < a.T ? lm_raw : 0ull;
   const uint64_t mine = readlane64(lm, t & (kWave - 1)) & a.rank_bits;

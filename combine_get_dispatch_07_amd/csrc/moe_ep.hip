@@ -459,6 +459,7 @@ const char* moe_status_string(moe_status status) {
     case MOE_ERR_CAPACITY: return "MOE_ERR_CAPACITY";
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
     case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: break;  // MOE_STATUS_MAX_ENUM and any other value
   }
   return "MOE_ERR_UNKNOWN";
 }
