@@ -570,15 +570,16 @@ def op_summary(bytes_: int, times_ms, kernel_us: float) -> dict:
 
     t = np.asarray(times_ms)
     mean_us = float(t.mean() * 1e3)
+    timed = kernel_us == kernel_us  # NaN: per-launch timing skipped
     return {
         "us_mean": round(mean_us, 3),
         "us_median": round(float(np.median(t) * 1e3), 3),
         "us_p10": round(float(np.percentile(t, 10) * 1e3), 3),
         "us_p90": round(float(np.percentile(t, 90) * 1e3), 3),
-        "us_kernel": round(kernel_us, 3),
+        "us_kernel": round(kernel_us, 3) if timed else None,
         "bytes": int(bytes_),
         "GB_per_s": round(bytes_ / (mean_us * 1e-6) / 1e9, 2),
-        "GB_per_s_kernel": round(bytes_ / (kernel_us * 1e-6) / 1e9, 2),
+        "GB_per_s_kernel": round(bytes_ / (kernel_us * 1e-6) / 1e9, 2) if timed else None,
         "frac_of_hbm_peak": round(bytes_ / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
     }
 
@@ -771,11 +772,13 @@ def main() -> int:
         copy_calibration(torch)
 
     ops = main_res["ops"]
-    dom = max(("dispatch", "combine"), key=lambda o: ops[o]["us_kernel"])
     # Per launch: HIP events on the launch stream around graphs of back-to-back launches of the kernel
     # (us_kernel), which is what a kernel trace reports as its duration.  The eager per-op events also
-    # hold each launch's gap (~2 us); their rate is reported beside it.
-    achieved = ops[dom]["GB_per_s_kernel"]
+    # hold each launch's gap (~2 us); their rate is reported beside it, and stands in for the
+    # per-launch one when that timing is skipped (--no-kernel-timing).
+    timed = not args.no_kernel_timing
+    dom = max(("dispatch", "combine"), key=lambda o: ops[o]["us_kernel"] if timed else ops[o]["us_mean"])
+    achieved = ops[dom]["GB_per_s_kernel"] if timed else ops[dom]["GB_per_s"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload, dom),
                 "algorithmic_bytes_per_launch": ops[dom]["bytes"], "launch_us": ops[dom]["us_kernel"],
