@@ -654,7 +654,9 @@ def copy_reference(torch, nbytes: int = 512 << 20, reps: int = 10) -> dict:
 
 
 HBM_CEILING = os.path.join(ROOT, "combine_get_dispatch_07_amd", "hbm_ceiling")
-CEILING_MIX = {"dispatch": "read1_write5", "combine": "read5_write1"}  # the kernels' read/write mixes
+# The probe's mix closest to each kernel's read/write mix
+CEILING_MIX = {"dispatch": "read1_write5", "combine": "read5_write1",
+               "combine_backward": "read5_write5", "dispatch_backward": "read5_write1"}
 
 
 def hbm_ceiling():
@@ -794,6 +796,12 @@ def main() -> int:
         best = ceiling[CEILING_MIX[dom]]["GB_per_s"]
         roofline["streaming_ceiling_same_mix"] = {"mix": CEILING_MIX[dom], "GB_per_s": best,
                                                   "frac": round(achieved / best, 4)}
+        for name, op in main_res.get("backward", {}).get("ops", {}).items():
+            rate = op.get("GB_per_s_kernel") or op["GB_per_s"]
+            best = ceiling.get(CEILING_MIX[name], {}).get("GB_per_s")
+            if best:
+                op["streaming_ceiling_same_mix"] = {"mix": CEILING_MIX[name], "GB_per_s": best,
+                                                    "frac": round(rate / best, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -6,7 +6,8 @@
 // not meet on the same HBM channels); the best of each mix is printed as one
 // JSON line.  Mixes: read only, write only, copy (1:1),
 // 5 reads : 1 write (the combine's mix at top-8 over 8 ranks, ~5.3 rows per
-// token) and 1 read : 5 writes (the dispatch's).  A measurement aid, not part
+// token), 1 read : 5 writes (the dispatch's) and 5 reads : 5 writes (close to
+// the combine backward's: g and the token's rows read, one row per rank written).  A measurement aid, not part
 // of the library: bench.py reports it next to the kernels' fraction of peak.
 //
 //   hipcc --offload-arch=gfx950 -O3 hbm_ceiling.hip -o hbm_ceiling && ./hbm_ceiling
@@ -134,7 +135,8 @@ int main() {
   if (measure<0, 1, 4>("write", src, dst, n, sink, e0, e1, false)) return 1;
   if (measure<1, 1, 4>("copy", src, dst, n, sink, e0, e1, false)) return 1;
   if (measure<5, 1, 2>("read5_write1", src, dst, n, sink, e0, e1, false)) return 1;
-  if (measure<1, 5, 2>("read1_write5", src, dst, n, sink, e0, e1, true)) return 1;
+  if (measure<1, 5, 2>("read1_write5", src, dst, n, sink, e0, e1, false)) return 1;
+  if (measure<5, 5, 1>("read5_write5", src, dst, n, sink, e0, e1, true)) return 1;
   printf("}\n");
   CHECK(hipDeviceSynchronize());
   CHECK(hipFree(src));
