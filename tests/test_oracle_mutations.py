@@ -19,7 +19,8 @@ from tests import test_oracle_router as PR
 
 
 def _pin_suite():
-    P.test_golden_layout_dispatch_combine()
+    P.test_golden_layout_dispatch_combine("hand_layout_dispatch_combine.json")
+    P.test_golden_layout_dispatch_combine("hand_duplicate_ids.json")
     P.test_golden_fp8_blocks()
     P.test_golden_combine_fp32_order()
     for case in P.TINY_CASES[:5]:
@@ -92,6 +93,39 @@ def _quant_no_floor(x_bits):
         v = (x / s[:, :, None]).astype(np.float32)
     v = np.nan_to_num(v)
     return N.e4m3_encode_rne(v).reshape(rows, H), s
+
+
+_orig_layout = O.get_dispatch_layout
+
+
+def _layout_experts_once_per_token(topk_idx, E, R):
+    tpr, _, mask = _orig_layout(topk_idx, E, R)
+    tpe = np.zeros(E, dtype=np.int32)
+    for row in topk_idx:
+        for e in set(int(v) for v in row if 0 <= v < E):
+            tpe[e] += 1
+    return tpr, tpe, mask
+
+
+def _layout_of_clamped_ids(topk_idx, E, R):
+    return _orig_layout(np.clip(topk_idx, 0, E - 1).astype(np.int32), E, R)
+
+
+def _quant_amax_per_row(x_bits):
+    rows, H = x_bits.shape
+    x = N.bf16_bits_to_f32(x_bits).reshape(rows, H // 128, 128)
+    a = np.repeat(np.abs(x).max(axis=(1, 2))[:, None], H // 128, axis=1)
+    s = (np.maximum(a, np.float32(1e-4)) / np.float32(448)).astype(np.float32)
+    v = (x / s[:, :, None]).astype(np.float32)
+    return N.e4m3_encode_rne(v).reshape(rows, H), s
+
+
+_orig_quant = O.quantize_fp8_blocks
+
+
+def _quant_stores_quantisation_scale(x_bits):
+    q, s = _orig_quant(x_bits)
+    return q, (np.float32(1.0) / s).astype(np.float32)
 
 
 _orig_combine = O.combine
@@ -290,6 +324,10 @@ MUTANTS = {
     "combine_reversed_slot_order": ("combine", _combine_reversed),
     "combine_fused_multiply_add": ("combine", _combine_fused),
     "metadata_global_expert_ids": ("dispatch_metadata", _meta_global_ids),
+    "expert_counts_once_per_token": ("get_dispatch_layout", _layout_experts_once_per_token),
+    "invalid_ids_clamped_not_skipped": ("get_dispatch_layout", _layout_of_clamped_ids),
+    "fp8_amax_per_row_not_per_block": ("quantize_fp8_blocks", _quant_amax_per_row),
+    "fp8_stores_quantisation_scale": ("quantize_fp8_blocks", _quant_stores_quantisation_scale),
 }
 
 

@@ -34,8 +34,9 @@ def _bf16_exact(values):
 
 # ---------------------------------------------------------------- golden, hand-worked
 
-def test_golden_layout_dispatch_combine():
-    g = json.load(open(os.path.join(GOLDEN, "hand_layout_dispatch_combine.json")))
+@pytest.mark.parametrize("fixture", ["hand_layout_dispatch_combine.json", "hand_duplicate_ids.json"])
+def test_golden_layout_dispatch_combine(fixture):
+    g = json.load(open(os.path.join(GOLDEN, fixture)))
     E, R = g["num_experts"], g["num_ranks"]
     idx = np.array(g["topk_idx"], dtype=np.int32)
     w = np.array(g["topk_w"], dtype=np.float32)
