@@ -139,3 +139,23 @@ def test_combine_backward_without_expert_rows():
     torch.cuda.synchronize()
     gw = gw_d.cpu().numpy()
     assert (gw.view(np.uint32) == 0).all()
+
+
+def test_dispatch_backward_rank_order_on_gpu():
+    """Hand case whose bf16 result depends on the order the rank rows are added (see
+    test_oracle_backward.test_dispatch_backward_rank_order): ascending order gives exactly 1.0."""
+    import combine_get_dispatch_07_amd as moe
+    from oracle.numerics import f32_to_bf16_bits_rne
+    from tests.gpu_harness import bf16_to_np
+    print("[case] dispatch backward rank order", flush=True)
+    idx = np.array([[0, 1, 2, 3]], np.int32)
+    send_row = np.array([[0, 1, 2, 3]], np.int32)
+    rows = f32_to_bf16_bits_rne(np.array([[1.0] * 8, [2.0 ** -8] * 8, [2.0 ** -24] * 8, [2.0 ** -24] * 8],
+                                         np.float32))
+    shape = moe.MoeShape(1, 8, 4, 4, 4)
+    gx_d = torch.empty((1, 8), dtype=torch.bfloat16, device="cuda")
+    gtw_d = torch.empty((1, 4), dtype=torch.float32, device="cuda")
+    moe.moe_dispatch_backward(shape, _dev(rows), _dev(idx), _dev(send_row), gx_d, _dev(np.zeros((4, 4), np.float32)),
+                              gtw_d)
+    torch.cuda.synchronize()
+    assert (bf16_to_np(gx_d) == 0x3F80).all()

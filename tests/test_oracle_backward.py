@@ -37,6 +37,24 @@ def test_golden_backward():
     assert gtw.tolist() == g["expect"]["grad_topk_w"]
 
 
+def test_dispatch_backward_rank_order():
+    """The rank rows of a token are added in ascending rank order, in fp32, then rounded to bf16.
+
+    Worked by hand: one token on four ranks (E = 4, R = 4, k = 4, expert r on rank r) whose receive
+    rows hold 1, 2^-8, 2^-24, 2^-24 (all exact in bf16).  Ascending: 1 + 2^-8 is exact; adding
+    2^-24 twice rounds back each time (a tie, to the even neighbour), so the sum is 1 + 2^-8, a bf16
+    tie that rounds to 1.0.  In descending order 2^-24 + 2^-24 = 2^-23 and the sum is
+    1 + 2^-8 + 2^-23 (exact in fp32), which rounds up to 1 + 2^-7 in bf16.
+    """
+    idx = np.array([[0, 1, 2, 3]], np.int32)
+    send_row, n = _layout(idx, 4, 4)
+    assert send_row.tolist() == [[0, 1, 2, 3]] and n == 4
+    rows = f32_to_bf16_bits_rne(np.array([[1.0] * 8, [2.0 ** -8] * 8, [2.0 ** -24] * 8, [2.0 ** -24] * 8],
+                                         np.float32))
+    gx, _ = O.dispatch_backward(rows, np.zeros((4, 4), np.float32), idx, send_row, 4, 4)
+    assert bf16_bits_to_f32(gx).tolist() == [[1.0] * 8]
+
+
 CASES = [(0, 1, 16, 8, 1, 1, 0.0), (1, 23, 16, 16, 4, 4, 0.2), (2, 40, 24, 32, 8, 8, 0.1), (3, 17, 16, 12, 3, 3, 0.3)]
 
 

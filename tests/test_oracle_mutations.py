@@ -31,6 +31,7 @@ def _pin_suite():
     P.test_identity_round_trip_weighted(P.W.CONFIG_BY_NAME["tiny"])
     PL.test_golden_low_latency()
     PB.test_golden_backward()
+    PB.test_dispatch_backward_rank_order()
     for case in PB.CASES:
         PB.test_backward_vs_bruteforce(case)
     for case in PL.LL_CASES[:3]:
@@ -126,6 +127,34 @@ _orig_quant = O.quantize_fp8_blocks
 def _quant_stores_quantisation_scale(x_bits):
     q, s = _orig_quant(x_bits)
     return q, (np.float32(1.0) / s).astype(np.float32)
+
+
+_orig_metadata = O.dispatch_metadata
+_orig_slots = O.assign_slots
+_orig_dbwd = O.dispatch_backward
+
+
+def _meta_keeps_other_ranks_weights(idx, w, E, R, send_row, n):
+    src, ridx, rw = _orig_metadata(idx, w, E, R, send_row, n)
+    valid = (idx >= 0) & (idx < E)
+    rw = np.where(valid[src], w[src], np.float32(0.0)).astype(np.float32) if n else rw
+    return src, ridx, rw
+
+
+def _slots_unsent_zero(mask):
+    offs, send, n = _orig_slots(mask)
+    return offs, np.where(send < 0, 0, send).astype(np.int32), n
+
+
+def _dbwd_descending_ranks(gr, grw, idx, send_row, E, R):
+    _, gw = _orig_dbwd(gr, grw, idx, send_row, E, R)
+    T = send_row.shape[0]
+    acc = np.zeros((T, gr.shape[1]), dtype=np.float32)
+    g = N.bf16_bits_to_f32(gr)
+    for r in reversed(range(send_row.shape[1])):
+        tt = np.nonzero(send_row[:, r] >= 0)[0]
+        acc[tt] = (acc[tt] + g[send_row[tt, r]]).astype(np.float32)
+    return N.f32_to_bf16_bits_rne(acc), gw
 
 
 _orig_combine = O.combine
@@ -328,6 +357,9 @@ MUTANTS = {
     "invalid_ids_clamped_not_skipped": ("get_dispatch_layout", _layout_of_clamped_ids),
     "fp8_amax_per_row_not_per_block": ("quantize_fp8_blocks", _quant_amax_per_row),
     "fp8_stores_quantisation_scale": ("quantize_fp8_blocks", _quant_stores_quantisation_scale),
+    "metadata_keeps_weights_of_other_ranks": ("dispatch_metadata", _meta_keeps_other_ranks_weights),
+    "unsent_send_row_zero": ("assign_slots", _slots_unsent_zero),
+    "dispatch_backward_descending_ranks": ("dispatch_backward", _dbwd_descending_ranks),
 }
 
 
