@@ -159,3 +159,22 @@ def test_dispatch_backward_rank_order_on_gpu():
                               gtw_d)
     torch.cuda.synchronize()
     assert (bf16_to_np(gx_d) == 0x3F80).all()
+
+
+def test_combine_backward_slot_order_on_gpu():
+    """Hand case whose bf16 grad_y depends on the order a rank's slots are added (see
+    test_oracle_backward.test_combine_backward_slot_order): ascending order gives exactly 1.0."""
+    import combine_get_dispatch_07_amd as moe
+    from oracle.numerics import f32_to_bf16_bits_rne
+    from tests.gpu_harness import bf16_to_np
+    print("[case] combine backward slot order", flush=True)
+    idx = np.array([[0, 1, 2, 3]], np.int32)
+    w = np.array([[1.0, 2.0 ** -8, 2.0 ** -24, 2.0 ** -24]], np.float32)
+    ones = f32_to_bf16_bits_rne(np.ones((1, 8), np.float32))
+    shape = moe.MoeShape(1, 8, 4, 4, 1)
+    gy_d = torch.empty((1, 8), dtype=torch.bfloat16, device="cuda")
+    gw_d = torch.empty((1, 4), dtype=torch.float32, device="cuda")
+    moe.moe_combine_backward(shape, _dev(ones), _dev(ones), _dev(idx), _dev(w), _dev(np.zeros((1, 1), np.int32)), gy_d,
+                             gw_d, num_y_rows=1)
+    torch.cuda.synchronize()
+    assert (bf16_to_np(gy_d) == 0x3F80).all()

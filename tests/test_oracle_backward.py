@@ -55,6 +55,23 @@ def test_dispatch_backward_rank_order():
     assert bf16_bits_to_f32(gx).tolist() == [[1.0] * 8]
 
 
+def test_combine_backward_slot_order():
+    """A rank row's gradient adds the token's slots on that rank in ascending slot order, in fp32.
+
+    Worked by hand: one token, four slots naming experts 0..3, all on the one rank (E = 4, R = 1),
+    g = 1 and weights 1, 2^-8, 2^-24, 2^-24: the products are exact and, as in the dispatch backward
+    case, ascending order gives 1 + 2^-8 (bf16: 1.0) where descending would give 1 + 2^-8 + 2^-23
+    (bf16: 1 + 2^-7).
+    """
+    idx = np.array([[0, 1, 2, 3]], np.int32)
+    w = np.array([[1.0, 2.0 ** -8, 2.0 ** -24, 2.0 ** -24]], np.float32)
+    send_row, n = _layout(idx, 4, 1)
+    assert send_row.tolist() == [[0]] and n == 1
+    g = f32_to_bf16_bits_rne(np.ones((1, 8), np.float32))
+    gy, _ = O.combine_backward(g, g.copy(), idx, w, send_row, 4, 1, 1)
+    assert bf16_bits_to_f32(gy).tolist() == [[1.0] * 8]
+
+
 CASES = [(0, 1, 16, 8, 1, 1, 0.0), (1, 23, 16, 16, 4, 4, 0.2), (2, 40, 24, 32, 8, 8, 0.1), (3, 17, 16, 12, 3, 3, 0.3)]
 
 

@@ -32,6 +32,7 @@ def _pin_suite():
     PL.test_golden_low_latency()
     PB.test_golden_backward()
     PB.test_dispatch_backward_rank_order()
+    PB.test_combine_backward_slot_order()
     for case in PB.CASES:
         PB.test_backward_vs_bruteforce(case)
     for case in PL.LL_CASES[:3]:
@@ -154,6 +155,21 @@ def _dbwd_descending_ranks(gr, grw, idx, send_row, E, R):
     for r in reversed(range(send_row.shape[1])):
         tt = np.nonzero(send_row[:, r] >= 0)[0]
         acc[tt] = (acc[tt] + g[send_row[tt, r]]).astype(np.float32)
+    return N.f32_to_bf16_bits_rne(acc), gw
+
+
+_orig_cbwd = O.combine_backward
+
+
+def _cbwd_descending_slots(g_bits, y_bits, idx, w, send_row, E, R, n):
+    _, gw = _orig_cbwd(g_bits, y_bits, idx, w, send_row, E, R, n)
+    valid, rank = O.expert_ranks(idx, E, R)
+    g = N.bf16_bits_to_f32(g_bits)
+    acc = np.zeros((n, g.shape[1]), dtype=np.float32)
+    for j in reversed(range(idx.shape[1])):
+        tt = np.nonzero(valid[:, j])[0]
+        rows = send_row[tt, rank[tt, j]]
+        acc[rows] = (acc[rows] + (w[tt, j][:, None].astype(np.float32) * g[tt]).astype(np.float32)).astype(np.float32)
     return N.f32_to_bf16_bits_rne(acc), gw
 
 
@@ -360,6 +376,7 @@ MUTANTS = {
     "metadata_keeps_weights_of_other_ranks": ("dispatch_metadata", _meta_keeps_other_ranks_weights),
     "unsent_send_row_zero": ("assign_slots", _slots_unsent_zero),
     "dispatch_backward_descending_ranks": ("dispatch_backward", _dbwd_descending_ranks),
+    "combine_backward_descending_slots": ("combine_backward", _cbwd_descending_slots),
 }
 
 
