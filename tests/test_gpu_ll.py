@@ -149,3 +149,33 @@ def test_combine_with_no_expert_rows_is_zero():
     out = H.run_combine(res["shape"], np.zeros((0, 256), np.uint16), res["_dev"]["idx"], res["_dev"]["w"],
                         res["_dev"]["d"]["send_row"], num_y_rows=0)
     assert (out == 0).all()
+
+
+def test_ll_combine_golden_fp32_order():
+    """tests/golden/hand_combine_fp32_order.json through the per-expert layout.  There E = R (one
+    expert per rank), so expert e's buffer holds exactly rank e's receive segment, in the same token
+    order: the expected bf16 outputs, which show the fp32 summation order and the absence of fused
+    multiply-add, are the same."""
+    import json
+    import os
+    import combine_get_dispatch_07_amd as moe
+    from oracle.numerics import f32_to_bf16_bits_rne
+    print("[case] ll golden fp32 order", flush=True)
+    g = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                    "hand_combine_fp32_order.json")))
+    E = g["num_experts"]
+    assert g["num_ranks"] == E
+    idx = np.array(g["topk_idx"], np.int32)
+    w = np.array(g["topk_w"], np.float32)
+    T, Hd = idx.shape[0], 8
+    count, slot_pos = O.ll_layout(idx, E)
+    rows = np.array(g["y_rows"], np.float32)
+    y = np.zeros((E, T, Hd), np.uint16)
+    first = np.concatenate([[0], np.cumsum(count)[:-1]])
+    for e in range(E):
+        y[e, :count[e]] = f32_to_bf16_bits_rne(rows[first[e]:first[e] + count[e], None] * np.ones((1, Hd), np.float32))
+    shape = moe.MoeShape(T, Hd, idx.shape[1], E, 1)
+    out = G().run_combine_ll(shape, y, torch.from_numpy(idx).cuda(), w, torch.from_numpy(slot_pos).cuda())
+    expect = f32_to_bf16_bits_rne(np.array(g["expect_out"], np.float32)[:, None] * np.ones((1, Hd), np.float32))
+    assert np.array_equal(out, expect)
+    assert np.array_equal(out, O.ll_combine(y, idx, w, slot_pos, E))

@@ -352,3 +352,27 @@ def test_layout_invariants_at_full_size():
     check_layout_invariants(idx, cfg.num_experts, cfg.num_ranks, res["tokens_per_rank"], res["tokens_per_expert"],
                             res["is_token_in_rank"])
     check_slot_invariants(res["is_token_in_rank"], res["rank_offsets"], res["send_row"], int(res["num_recv"][0]))
+
+
+def test_combine_golden_fp32_order():
+    """The hand-worked fixture in which the fp32 summation order and the absence of fused
+    multiply-add show in the bf16 output (tests/golden/hand_combine_fp32_order.json), on the GPU."""
+    import json
+    import os
+    import combine_get_dispatch_07_amd as moe
+    _print_case("edge", name="golden_fp32_order")
+    g = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                    "hand_combine_fp32_order.json")))
+    E, R = g["num_experts"], g["num_ranks"]
+    idx = np.array(g["topk_idx"], np.int32)
+    w = np.array(g["topk_w"], np.float32)
+    _, _, mask = O.get_dispatch_layout(idx, E, R)
+    _, send_row, n = O.assign_slots(mask)
+    Hd = 8
+    y = f32_to_bf16_bits_rne(np.array(g["y_rows"], np.float32)[:, None] * np.ones((1, Hd), np.float32))
+    assert y.shape[0] == n
+    shape = moe.MoeShape(idx.shape[0], Hd, idx.shape[1], E, R)
+    out = H().run_combine(shape, y, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda(),
+                          torch.from_numpy(send_row).cuda())
+    expect = f32_to_bf16_bits_rne(np.array(g["expect_out"], np.float32)[:, None] * np.ones((1, Hd), np.float32))
+    assert np.array_equal(out, expect)
