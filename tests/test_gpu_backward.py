@@ -178,3 +178,41 @@ def test_combine_backward_slot_order_on_gpu():
                              gw_d, num_y_rows=1)
     torch.cuda.synchronize()
     assert (bf16_to_np(gy_d) == 0x3F80).all()
+
+
+def test_golden_backward_on_gpu():
+    """tests/golden/hand_backward.json (on the forward fixture hand_layout_dispatch_combine.json)
+    through moe_combine_backward / moe_dispatch_backward.  The fixture's 2-channel rows are repeated
+    to 8 channels, so the weight gradients (dot products over the channels) are 4 times the
+    fixture's; every value involved is small and exact in fp32."""
+    import json
+    import os
+    import combine_get_dispatch_07_amd as moe
+    from oracle.numerics import f32_to_bf16_bits_rne
+    from tests.gpu_harness import bf16_to_np
+    print("[case] backward golden hand case", flush=True)
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    fwd = json.load(open(os.path.join(here, "hand_layout_dispatch_combine.json")))
+    ex = json.load(open(os.path.join(here, "hand_backward.json")))["expect"]
+    E, R = fwd["num_experts"], fwd["num_ranks"]
+    idx = np.array(fwd["topk_idx"], np.int32)
+    w = np.array(fwd["topk_w"], np.float32)
+    send_row = np.array(fwd["expect"]["send_row"], np.int32)
+    n = fwd["expect"]["num_recv"]
+    T, k, Hd = idx.shape[0], idx.shape[1], 8
+    g = f32_to_bf16_bits_rne(np.tile(np.array([[t + 1, -(t + 1)] for t in range(T)], np.float32), (1, Hd // 2)))
+    y = f32_to_bf16_bits_rne(np.tile(np.array([[i + 1, -(i + 1) / 2] for i in range(n)], np.float32), (1, Hd // 2)))
+    grw = np.array([[10 * i + j for j in range(k)] for i in range(n)], np.float32)
+    shape = moe.MoeShape(T, Hd, k, E, R)
+    gy_d = torch.empty((n, Hd), dtype=torch.bfloat16, device="cuda")
+    gw_d = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_combine_backward(shape, _dev(g), _dev(y), _dev(idx), _dev(w), _dev(send_row), gy_d, gw_d, num_y_rows=n)
+    gx_d = torch.empty((T, Hd), dtype=torch.bfloat16, device="cuda")
+    gtw_d = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_dispatch_backward(shape, _dev(y), _dev(idx), _dev(send_row), gx_d, _dev(grw), gtw_d)
+    torch.cuda.synchronize()
+    tile = lambda a: f32_to_bf16_bits_rne(np.tile(np.array(a, np.float32), (1, Hd // 2)))  # noqa: E731
+    assert np.array_equal(bf16_to_np(gy_d), tile(ex["grad_y"]))
+    assert gw_d.cpu().numpy().tolist() == (4 * np.array(ex["grad_w"], np.float32)).tolist()
+    assert np.array_equal(bf16_to_np(gx_d), tile(ex["grad_x"]))
+    assert gtw_d.cpu().numpy().tolist() == ex["grad_topk_w"]

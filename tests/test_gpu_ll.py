@@ -179,3 +179,35 @@ def test_ll_combine_golden_fp32_order():
     expect = f32_to_bf16_bits_rne(np.array(g["expect_out"], np.float32)[:, None] * np.ones((1, Hd), np.float32))
     assert np.array_equal(out, expect)
     assert np.array_equal(out, O.ll_combine(y, idx, w, slot_pos, E))
+
+
+def test_ll_golden_hand_case():
+    """tests/golden/hand_low_latency.json through moe_dispatch_ll / moe_combine_ll, against the values
+    derived by hand (the fixture's 2-channel expert outputs repeated to 8 channels)."""
+    import json
+    import os
+    from oracle.numerics import f32_to_bf16_bits_rne
+    print("[case] ll golden hand case", flush=True)
+    g = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_low_latency.json")))
+    E, cap, ex = g["num_experts"], g["capacity"], g["expect"]
+    idx = np.array(g["topk_idx"], np.int32)
+    w = np.array(g["topk_w"], np.float32)
+    T = idx.shape[0]
+    x = f32_to_bf16_bits_rne(np.arange(T * 128, dtype=np.float32).reshape(T, 128) / 64)
+    res = G().run_dispatch_ll(x, idx, E, cap, "bf16")
+    assert res["recv_count"].tolist() == ex["recv_count"]
+    assert res["slot_pos"].tolist() == ex["slot_pos"]
+    for e in range(E):
+        n = ex["recv_count"][e]
+        assert res["recv_src_idx"][e, :n].tolist() == ex["recv_src_idx"][e][:n], e
+        assert np.array_equal(res["recv_x"][e, :n], x[ex["recv_src_idx"][e][:n]]), e
+    Hd = 8
+    y = np.zeros((E, cap, Hd), np.float32)
+    for e in range(E):
+        for p in range(cap):
+            y[e, p] = [e + 1 + 8 * p, -(e + 1) / 2 - p] * (Hd // 2)
+    import combine_get_dispatch_07_amd as moe
+    shape = moe.MoeShape(T, Hd, idx.shape[1], E, 1)
+    out = G().run_combine_ll(shape, f32_to_bf16_bits_rne(y), res["_dev"]["idx"], w, res["_dev"]["d"]["slot_pos"])
+    expect = f32_to_bf16_bits_rne(np.tile(np.array(ex["combine_out"], np.float32), (1, Hd // 2)))
+    assert np.array_equal(out, expect)

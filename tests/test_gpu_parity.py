@@ -407,3 +407,23 @@ def test_golden_hand_cases(fixture):
     out = H().run_combine(res["shape"], y, dev["idx"], dev["w"], dev["d"]["send_row"])
     expect = f32_to_bf16_bits_rne(np.tile(np.array(ex["combine_out"], np.float32), (1, Hd // 2)))
     assert np.array_equal(out, expect)
+
+
+def test_golden_fp8_blocks():
+    """tests/golden/hand_fp8_blocks.json (codes and scales worked out by hand, ties included) through
+    an FP8 dispatch of one token per block on the GPU."""
+    import json
+    import os
+    _print_case("golden", name="hand_fp8_blocks")
+    g = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_fp8_blocks.json")))
+    for blk in g["blocks"]:
+        vals = np.zeros(128, np.float32)
+        vals[:len(blk["values"])] = blk["values"]
+        codes = np.zeros(128, np.uint8)
+        codes[:len(blk["codes"])] = blk["codes"]
+        x = f32_to_bf16_bits_rne(vals)[None, :]
+        assert np.array_equal(bf16_bits_to_f32(x)[0], vals), blk["name"]  # the values are exact in bf16
+        res = H().run_layout_dispatch(x, np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32), 1, 1, "fp8")
+        assert int(res["num_recv"][0]) == 1
+        assert res["recv_x"][0].tolist() == codes.tolist(), blk["name"]
+        assert res["recv_scales"][0].tolist() == [blk["scale"]], blk["name"]

@@ -159,3 +159,29 @@ def test_route_deterministic():
     b = H().run_route(logits, 8, 256, 8, "softmax")
     assert np.array_equal(a["topk_idx"], b["topk_idx"])
     assert np.array_equal(a["topk_w"].view(np.uint32), b["topk_w"].view(np.uint32))
+
+
+def test_route_golden_hand_cases():
+    """tests/golden/hand_router.json (ids picked by hand, weights as closed forms) through
+    moe_route_layout: ids bit-exact, weights within the fp32 bound of the closed-form values."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_router.json")))
+    for case in g["cases"]:
+        _print_case("golden", case=case["label"][:40].replace(" ", "_"))
+        logits = np.array(case["logits"], np.float32)
+        T, E, k, G = logits.shape[0], logits.shape[1], case["k"], case["num_groups"]
+        # The router needs E % 8 == 0: pad every group with experts no token can pick (logit -1e30),
+        # which leaves the groups, their scores and the picks unchanged; ids map e -> e' below.
+        E2 = -(-E // 8) * 8
+        L, L2 = E // G, E2 // G
+        new_id = np.array([(e // L) * L2 + e % L for e in range(E)])
+        padded = np.full((T, E2), -1e30, np.float32)
+        padded[:, new_id] = logits
+        res = H().run_route(padded, k, E2, 1, case["gate"], G, case["topk_groups"])
+        back = {int(n): e for e, n in enumerate(new_id)}
+        ids = [[back.get(int(v), -1) for v in row] for row in res["topk_idx"]]
+        assert ids == case["topk_idx"], case["label"]
+        ref = np.array(case["topk_w"], np.float64)
+        rel = np.abs(res["topk_w"].astype(np.float64) - ref) / np.abs(ref)
+        assert (rel <= weight_bound(padded, res["topk_idx"], k, case["gate"])).all(), case["label"]
