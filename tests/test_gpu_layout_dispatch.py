@@ -115,7 +115,24 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def _random_shapes(n: int, seed: int = 0x5E1D):
+    """Seeded shapes for the one-kernel path (T <= 1024, hidden <= 16384) inside the limits."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([1, 2, 3, 4, 6, 8, 16, 32, 64]))
+        L = int(rng.integers(1, max(2, 512 // R) + 1))
+        E = R * L
+        k = int(rng.integers(1, min(E, 32) + 1))
+        dtype = "fp8" if rng.random() < 0.5 else "bf16"
+        H = 128 * int(rng.integers(1, 17)) if dtype == "fp8" else 8 * int(rng.integers(1, 257))
+        T = int(rng.integers(1, 1025))
+        inv = float(rng.choice([0.0, 0.1, 0.4]))
+        out.append((f"rand{i}_T{T}_H{H}_E{E}_k{k}_R{R}_{dtype}", 400 + i, T, H, E, k, R, dtype, inv))
+    return out
+
+
+@pytest.mark.parametrize("case", CASES + _random_shapes(8), ids=lambda c: c[0])
 def test_layout_dispatch_edges(case):
     name, seed, T, H, E, k, R, dtype, inv = case
     d = W.random_case(seed, T, H, E, k, R, invalid_frac=inv)
