@@ -122,7 +122,28 @@ EDGES = [  # (label, T, E, k, R, gate, G, KG, ties, misalign)
 ]
 
 
-@pytest.mark.parametrize("case", EDGES, ids=lambda c: c[0])
+def _random_shapes(n: int, seed: int = 0x70E):
+    """Seeded router shapes inside the limits: E % 8 == 0, k <= 16, G in {1, 2, 4, 8},
+    k <= topk_groups * E / G, R | E."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        E = 8 * int(rng.integers(1, 129))
+        G = int(rng.choice([1, 2, 4, 8]))
+        if E % G:
+            continue
+        KG = int(rng.integers(1, G + 1))
+        k = int(rng.integers(1, min(16, KG * (E // G)) + 1))
+        Rs = [r for r in (1, 2, 4, 8, 16, 32, 64) if E % r == 0 and r <= E]
+        R = int(rng.choice(Rs))
+        T = int(rng.integers(1, 3000))
+        gate = "softmax" if rng.random() < 0.5 else "sigmoid"
+        ties = bool(rng.random() < 0.5)
+        out.append((f"rand{len(out)}_T{T}_E{E}_k{k}_G{G}_KG{KG}_R{R}", T, E, k, R, gate, G, KG, ties, False))
+    return out
+
+
+@pytest.mark.parametrize("case", EDGES + _random_shapes(8), ids=lambda c: c[0])
 def test_route_edges(case):
     label, T, E, k, R, gate, G, KG, ties, misalign = case
     _print_case(label, T=T, E=E, k=k, R=R, gate=gate, G=G, KG=KG, ties=ties, misalign=misalign)
