@@ -19,6 +19,8 @@ from tests import test_oracle_router as PR
 
 
 def _pin_suite():
+    P.test_golden_dequant_bf16()
+    P.test_combine_f64_closed_form()
     P.test_golden_layout_dispatch_combine("hand_layout_dispatch_combine.json")
     P.test_golden_layout_dispatch_combine("hand_duplicate_ids.json")
     P.test_golden_fp8_blocks()
@@ -95,6 +97,45 @@ def _quant_no_floor(x_bits):
         v = (x / s[:, :, None]).astype(np.float32)
     v = np.nan_to_num(v)
     return N.e4m3_encode_rne(v).reshape(rows, H), s
+
+
+def _dequant_rounded(q, s, to_bf16):
+    rows, H = q.shape
+    v = N.e4m3_decode(q).reshape(rows, H // 128, 128) * s[:, :, None]
+    return to_bf16(v.astype(np.float32).reshape(rows, H))
+
+
+def _dequant_truncates(q, s):
+    return _dequant_rounded(q, s, _bf16_truncate)
+
+
+def _dequant_ties_away(q, s):
+    def half_away(x):
+        u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+        return ((u + np.uint64(0x8000)) >> np.uint64(16)).astype(np.uint16)
+    return _dequant_rounded(q, s, half_away)
+
+
+def _combine_f64_in_fp32(y, idx, w, send_row, E, R, tokens=None):
+    valid, rank = O.expert_ranks(idx, E, R)
+    t_sel = np.arange(idx.shape[0]) if tokens is None else np.asarray(tokens)
+    acc = np.zeros((t_sel.size, y.shape[1]), dtype=np.float32)
+    mag = np.zeros((t_sel.size, y.shape[1]), dtype=np.float32)
+    for j in range(idx.shape[1]):
+        ok = valid[t_sel, j]
+        tj = t_sel[ok]
+        p = w[tj, j][:, None] * N.bf16_bits_to_f32(y[send_row[tj, rank[tj, j]]])
+        acc[ok] += p
+        mag[ok] += np.abs(p)
+    return acc.astype(np.float64), mag.astype(np.float64)
+
+
+_orig_combine_f64 = O.combine_f64
+
+
+def _combine_f64_signed_magnitude(y, idx, w, send_row, E, R, tokens=None):
+    acc, _ = _orig_combine_f64(y, idx, w, send_row, E, R, tokens)
+    return acc, np.abs(acc)
 
 
 _orig_layout = O.get_dispatch_layout
@@ -352,6 +393,10 @@ def test_router_pins_catch_mutant(name, monkeypatch):
 
 
 MUTANTS = {
+    "dequant_bf16_truncates": ("dequantize_fp8_to_bf16", _dequant_truncates),
+    "dequant_bf16_ties_away": ("dequantize_fp8_to_bf16", _dequant_ties_away),
+    "combine_f64_accumulates_in_fp32": ("combine_f64", _combine_f64_in_fp32),
+    "combine_f64_magnitude_of_sum": ("combine_f64", _combine_f64_signed_magnitude),
     "dispatch_backward_drops_last_rank": ("dispatch_backward", _dbwd_drop_last_rank),
     "dispatch_backward_weight_slot": ("dispatch_backward", _dbwd_weight_of_first_slot),
     "combine_backward_unweighted": ("combine_backward", _cbwd_unweighted),

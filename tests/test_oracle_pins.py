@@ -307,3 +307,48 @@ def test_fp8_identity_round_trip():
     # per-element E4M3 error (2^-4 relative + subnormal floor) survives the convex combination
     blk_amax = np.abs(xf).reshape(16, -1, 128).max(axis=2).repeat(128, axis=1)
     assert (np.abs(got - xf) <= 2.0 ** -4 * np.abs(xf) + 2.0 ** -10 * blk_amax / 448 * 2 + 2.0 ** -7 * np.abs(xf)).all()
+
+
+def test_golden_dequant_bf16():
+    """tests/golden/hand_dequant_bf16.json: the identity expert on FP8 rows, BF16_RNE(fl32(decode(q) * s)),
+    on products that land on or next to bf16 midpoints (ties to even up and down, a negative tie, a
+    subnormal code), worked out by hand."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_dequant_bf16.json")))
+    cases = g["cases"]
+    q = np.zeros((len(cases), 128), np.uint8)
+    s = np.zeros((len(cases), 1), np.float32)
+    for i, c in enumerate(cases):
+        q[i, 0] = c["code"]
+        s[i, 0] = c["scale"]
+        assert float(np.float32(c["scale"])) == c["scale"], c["name"]  # the scales are exact in fp32
+    y = O.dequantize_fp8_to_bf16(q, s)
+    assert y[:, 0].tolist() == [c["bf16"] for c in cases]
+    assert (y[:, 1:] == 0).all()  # code 0x00 -> +0
+
+
+def test_combine_f64_closed_form():
+    """combine_f64 returns the exact weighted sum and the sum of magnitudes.  Closed forms:
+    token 0: w = (1, 1, 1) on rows (2^24, 1, -2^24) -> exact sum 1 (an fp32 running sum gives 0:
+    2^24 + 1 rounds to 2^24), magnitude 2^25 + 1; token 1: w = (0.5, 0.25) on rows (3, -5) and an
+    invalid third slot -> 0.5*3 - 0.25*5 = 0.25, magnitude 1.5 + 1.25 = 2.75."""
+    E, R = 4, 4  # one expert per rank: expert e's row is the token's row on rank e
+    idx = np.array([[0, 1, 2], [1, 3, -1]], np.int32)
+    w = np.array([[1.0, 1.0, 1.0], [0.5, 0.25, 0.75]], np.float32)
+    _, _, mask = O.get_dispatch_layout(idx, E, R)
+    _, send_row, n = O.assign_slots(mask)
+    # ranks: token 0 -> 0, 1, 2; token 1 -> 1, 3; segment sizes 1, 2, 1, 1
+    assert n == 5 and send_row.tolist() == [[0, 1, 3, -1], [-1, 2, -1, 4]]
+    rows = np.zeros((n, 2), np.float32)
+    rows[send_row[0, 0]] = 2.0 ** 24
+    rows[send_row[0, 1]] = 1.0
+    rows[send_row[0, 2]] = -(2.0 ** 24)
+    rows[send_row[1, 1]] = 3.0
+    rows[send_row[1, 3]] = -5.0
+    y = _bf16_exact(rows)
+    acc, mag = O.combine_f64(y, idx, w, send_row, E, R)
+    assert acc.dtype == np.float64 and mag.dtype == np.float64
+    assert acc[:, 0].tolist() == [1.0, 0.25] and acc[:, 1].tolist() == [1.0, 0.25]
+    assert mag[:, 0].tolist() == [2.0 ** 25 + 1, 2.75]
+    assert O.combine_f64(y, idx, w, send_row, E, R, tokens=np.array([1]))[0][:, 0].tolist() == [0.25]
+    # the fp32-sequenced oracle differs here by exactly the lost 1
+    assert bf16_bits_to_f32(O.combine(y, idx, w, send_row, E, R))[:, 0].tolist() == [0.0, 0.25]
