@@ -62,77 +62,97 @@ def check_metadata_and_guards(res, idx, w, E, R, send_row, n):
     return src
 
 
-def check_payload(res, x, src, n, dtype, sample_tokens=None):
+def check_payload(res, x, src, n, dtype):
+    """Every receive row against the oracle.  bf16: the oracle's bit copy of the source row.  FP8:
+    the oracle's dispatch quantises each receive row, and the quantisation is a function of the row
+    alone, so at large sizes each source token is quantised once (in token chunks, to bound host
+    memory) and every receive row is compared with its source token's codes and scales."""
     if dtype == "bf16":
-        if sample_tokens is None:
-            assert np.array_equal(res["recv_x"][:n], O.dispatch_rows_bf16(x, src))
-        else:
-            rows = np.nonzero(np.isin(src, sample_tokens))[0]
-            assert np.array_equal(res["recv_x"][rows], O.dispatch_rows_bf16(x, src[rows]))
+        assert np.array_equal(res["recv_x"][:n], O.dispatch_rows_bf16(x, src))
         return
-    toks = np.arange(x.shape[0]) if sample_tokens is None else np.asarray(sample_tokens)
-    q_tok, s_tok = O.quantize_fp8_blocks(x[toks])
-    pos = np.full(x.shape[0], -1, dtype=np.int64)
-    pos[toks] = np.arange(toks.size)
-    rows = np.nonzero(pos[src] >= 0)[0]
-    got_q = res["recv_x"][rows]
-    got_s = res["recv_scales"][rows]
-    exp_q = q_tok[pos[src[rows]]]
-    exp_s = s_tok[pos[src[rows]]]
-    bad = np.nonzero((got_q != exp_q).any(axis=1))[0]
-    assert bad.size == 0, f"fp8 bytes differ in {bad.size} rows, first row {rows[bad[0]]}"
-    assert np.array_equal(got_s.view(np.uint32), exp_s.view(np.uint32))
+    got_q, got_s = res["recv_x"][:n], res["recv_scales"][:n]
+    if n * x.shape[1] <= 50_000_000:
+        exp_q, exp_s = O.dispatch_rows_fp8(x, src)
+        bad = np.nonzero((got_q != exp_q).any(axis=1))[0]
+        assert bad.size == 0, f"fp8 bytes differ in {bad.size} rows, first row {bad[:1]}"
+        assert np.array_equal(got_s.view(np.uint32), exp_s.view(np.uint32))
+        return
+    T, step, seen = x.shape[0], 2048, 0
+    for t0 in range(0, T, step):
+        t1 = min(T, t0 + step)
+        rows = np.nonzero((src >= t0) & (src < t1))[0]
+        q_tok, s_tok = O.quantize_fp8_blocks(x[t0:t1])
+        bad = np.nonzero((got_q[rows] != q_tok[src[rows] - t0]).any(axis=1))[0]
+        assert bad.size == 0, f"fp8 bytes differ in {bad.size} rows, first row {rows[bad[0]]}"
+        assert np.array_equal(got_s[rows].view(np.uint32), s_tok[src[rows] - t0].view(np.uint32))
+        seen += rows.size
+    assert seen == n
 
 
-def check_combine(res, y, idx, w, E, R, send_row, tokens=None, num_y_rows=None):
+def check_combine(res, y, idx, w, E, R, send_row, num_y_rows=None, bound_sample=None):
+    """All T outputs against the oracle's fp32 combine (gate: 1 bf16 ulp; returns whether they are
+    bit-identical).  The fp64 sanity bound is checked on every token, or on `bound_sample` tokens."""
     dev = res["_dev"]
     out = H().run_combine(res["shape"], y, dev["idx"], dev["w"], dev["d"]["send_row"], num_y_rows=num_y_rows)
-    toks = np.arange(idx.shape[0]) if tokens is None else np.asarray(tokens)
-    ref = O.combine(y, idx, w, send_row, E, R, tokens=toks)
-    got = out[toks]
-    ok = within_one_bf16_ulp(got, ref)
+    ref = O.combine(y, idx, w, send_row, E, R)
+    ok = within_one_bf16_ulp(out, ref)
     assert ok.all(), f"{(~ok).sum()} combine outputs beyond 1 bf16 ulp"
-    exact = np.array_equal(got, ref)
+    exact = np.array_equal(out, ref)
+    toks = np.arange(idx.shape[0]) if bound_sample is None else np.asarray(bound_sample)
     ref64, mag = O.combine_f64(y, idx, w, send_row, E, R, tokens=toks)
-    check_combine_bound(got, ref64, mag, idx.shape[1])
+    check_combine_bound(out[toks], ref64, mag, idx.shape[1])
     return out, exact
 
 
-def run_case(x, idx, w, E, R, dtype, y=None, sample_tokens=None, combine_tokens=None, identity=False):
+def run_case(x, idx, w, E, R, dtype, y=None, identity=False, bound_sample=None, combine=True):
     res = H().run_layout_dispatch(x, idx, w, E, R, dtype)
     send_row, n = check_layout_and_slots(res, idx, E, R)
     src = check_metadata_and_guards(res, idx, w, E, R, send_row, n)
-    check_payload(res, x, src, n, dtype, sample_tokens)
+    check_payload(res, x, src, n, dtype)
     exact = None
     if identity:
         if dtype == "bf16":
             y = res["recv_x"][:n]
         else:
             y = O.dequantize_fp8_to_bf16(res["recv_x"][:n], res["recv_scales"][:n])
-    if y is not None:
-        _, exact = check_combine(res, y, idx, w, E, R, send_row, tokens=combine_tokens)
+    if y is not None and combine:
+        _, exact = check_combine(res, y, idx, w, E, R, send_row, bound_sample=bound_sample)
     return res, exact
 
 
 # ------------------------------------------------------------------ the five workloads
 
-@pytest.mark.parametrize("cfg", W.CONFIGS, ids=lambda c: c.name)
-def test_workload_parity(cfg):
-    _print_case("workload", name=cfg.name, T=cfg.num_tokens, H=cfg.hidden, E=cfg.num_experts,
-                k=cfg.num_topk, R=cfg.num_ranks, dtype=cfg.dispatch_dtype)
+def _workload(cfg):
     d = W.make_inputs(cfg)
-    x, idx, w = d["x"], d["topk_idx"], d["topk_w"]
+    return d["x"], d["topk_idx"], d["topk_w"]
+
+
+@pytest.mark.parametrize("cfg", W.CONFIGS, ids=lambda c: c.name)
+def test_workload_dispatch_parity(cfg):
+    """Full size: layout, slots, metadata and every receive row (bf16 bits, or FP8 codes and scales)."""
+    _print_case("workload-dispatch", name=cfg.name, T=cfg.num_tokens, H=cfg.hidden, E=cfg.num_experts,
+                k=cfg.num_topk, R=cfg.num_ranks, dtype=cfg.dispatch_dtype)
+    x, idx, w = _workload(cfg)
+    run_case(x, idx, w, cfg.num_experts, cfg.num_ranks, cfg.dispatch_dtype, combine=False)
+
+
+@pytest.mark.parametrize("cfg", W.CONFIGS, ids=lambda c: c.name)
+def test_workload_combine_parity(cfg):
+    """Full size: all T combine outputs against the oracle (bit-identical expected, 1 bf16 ulp gate)."""
+    _print_case("workload-combine", name=cfg.name, T=cfg.num_tokens, H=cfg.hidden, E=cfg.num_experts,
+                k=cfg.num_topk, R=cfg.num_ranks, dtype=cfg.dispatch_dtype)
+    x, idx, w = _workload(cfg)
     E, R, T = cfg.num_experts, cfg.num_ranks, cfg.num_tokens
-    big = T * cfg.hidden > 8_000_000
-    rng = np.random.default_rng(cfg.index)
-    sample = np.sort(rng.choice(T, size=min(T, 384), replace=False)) if big else None
-    y = None
-    if cfg.combine_input == "random":
-        _, _, mask = O.get_dispatch_layout(idx, E, R)
-        n = int(mask.sum())
+    res = H().run_layout_dispatch(x, idx, w, E, R, cfg.dispatch_dtype)
+    send_row, n = check_layout_and_slots(res, idx, E, R)
+    if cfg.combine_input == "identity":
+        y = res["recv_x"][:n] if cfg.dispatch_dtype == "bf16" else \
+            O.dequantize_fp8_to_bf16(res["recv_x"][:n], res["recv_scales"][:n])
+    else:
         y = W.draw_expert_outputs(W.y_stream(cfg), n, cfg.hidden)
-    _, exact = run_case(x, idx, w, E, R, cfg.dispatch_dtype, y=y, sample_tokens=sample, combine_tokens=sample,
-                        identity=cfg.combine_input == "identity")
+    big = T * cfg.hidden > 8_000_000
+    sample = np.sort(np.random.default_rng(cfg.index).choice(T, size=1024, replace=False)) if big else None
+    _, exact = check_combine(res, y, idx, w, E, R, send_row, bound_sample=sample)
     assert exact, "combine not bit-identical to the fp32-sequenced oracle"
 
 
@@ -158,6 +178,13 @@ EDGE = [
     ("one_expert_per_rank_k_eq_E", 16, 513, 256, 8, 8, 8, "bf16", 0.0),  # L = 1, every token to every rank
     ("min_hidden_bf16", 17, 1500, 8, 32, 4, 8, "bf16", 0.05),   # one 16-byte piece per row
     ("min_hidden_fp8", 18, 1500, 128, 32, 4, 8, "fp8", 0.05),   # one scale block per row
+    # FP8 at hidden 7168 (14 groups of 64 16-byte pieces): the host takes the widest slice of
+    # 14, 7, 4, 2 groups that still gives >= 4096 waves (T * slices), so each batch size below
+    # runs a different dispatch width: 700 tokens -> 2 groups, 1500 -> 4, 3000 -> 7, 4100 -> 14.
+    ("fp8_h7168_width2", 19, 700, 7168, 256, 8, 8, "fp8", 0.02),
+    ("fp8_h7168_width4", 20, 1500, 7168, 256, 8, 8, "fp8", 0.02),
+    ("fp8_h7168_width7", 21, 3000, 7168, 256, 8, 32, "fp8", 0.02),
+    ("fp8_h7168_width14_ragged", 22, 4100, 7168, 128, 8, 16, "fp8", 0.05),
 ]
 
 
@@ -335,11 +362,15 @@ def test_run_to_run_identical():
     for key in ("tokens_per_rank", "tokens_per_expert", "is_token_in_rank", "send_row", "recv_x", "recv_scales",
                 "recv_src_idx", "recv_topk_idx", "recv_topk_w"):
         assert np.array_equal(a[key], b[key]), key
-    n = int(a["num_recv"][0])
+    # and both runs against the oracle (1500 tokens at hidden 7168 runs the 4-group FP8 width)
+    send_row, n = check_layout_and_slots(a, d["topk_idx"], c.num_experts, c.num_ranks)
+    src = check_metadata_and_guards(a, d["topk_idx"], d["topk_w"], c.num_experts, c.num_ranks, send_row, n)
+    check_payload(a, d["x"], src, n, "fp8")
     y = W.draw_expert_outputs(np.random.default_rng(3), n, c.hidden)
     o1 = H().run_combine(a["shape"], y, a["_dev"]["idx"], a["_dev"]["w"], a["_dev"]["d"]["send_row"])
     o2 = H().run_combine(a["shape"], y, a["_dev"]["idx"], a["_dev"]["w"], a["_dev"]["d"]["send_row"])
     assert np.array_equal(o1, o2)
+    assert np.array_equal(o1, O.combine(y, d["topk_idx"], d["topk_w"], send_row, c.num_experts, c.num_ranks))
 
 
 def test_layout_invariants_at_full_size():
