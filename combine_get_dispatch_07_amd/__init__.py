@@ -26,7 +26,9 @@ def alloc_layout(shape: MoeShape, device="cuda") -> Dict[str, torch.Tensor]:
         "tokens_per_rank": torch.empty(shape.num_ranks, dtype=torch.int32, device=device),
         "tokens_per_expert": torch.empty(shape.num_experts, dtype=torch.int32, device=device),
         "is_token_in_rank": torch.empty((shape.num_tokens, shape.num_ranks), dtype=torch.uint8, device=device),
-        "workspace": torch.empty(workspace_bytes(shape), dtype=torch.uint8, device=device),
+        # zero-filled once: its first words coordinate the blocks of a launch and every call
+        # leaves them zero again
+        "workspace": torch.zeros(workspace_bytes(shape), dtype=torch.uint8, device=device),
     }
 
 

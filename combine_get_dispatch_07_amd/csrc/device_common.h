@@ -110,4 +110,31 @@ __device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, kHi);
 }
 
+// Hand-off of data between the blocks of one launch.  On gfx950 every XCD has
+// its own L2, and an agent-scope release or acquire fence writes back or
+// invalidates a whole L2, which is slow.  So data one block hands to another is
+// written and read with agent-scope atomic stores and loads (relaxed), which go
+// through the L2 to the device-coherent level (the sc1 bit), and ordering comes
+// from waits alone: a writer waits for its own stores to complete before the
+// atomic that signals them (wait_own_stores), and a reader issues its loads
+// only once the signalling atomic's value has arrived.  Nothing else of the
+// block needs to reach another block in the same launch.
+template <typename T>
+__device__ __forceinline__ void put_coherent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ T get_coherent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// This wave's earlier vector-memory operations (stores and atomics included)
+// have completed: s_waitcnt vmcnt(0), with the expcnt and lgkmcnt fields at
+// their "no wait" maxima (7 and 15).
+__device__ __forceinline__ void wait_own_stores() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+}
+
 }  // namespace moe

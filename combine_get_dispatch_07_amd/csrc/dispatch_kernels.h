@@ -40,7 +40,7 @@ struct DispatchArgs {
   const int32_t* topk_idx;
   const float* topk_w;
   const uint64_t* token_ranks;
-  const int32_t* chunk_base;
+  const int32_t* chunk_base;     // [R, NC] receive row of each chunk's first token on rank r
   const int32_t* ws_rank_offsets;
   void* recv_x;
   float* recv_scales;
@@ -158,10 +158,10 @@ __device__ __forceinline__ void dispatch_item(const DispatchArgs& a, int item, i
   const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H);
   const int jl = min(lane, a.k - 1);
 
-  // All loads first: the chunk's rank bitmasks (one per lane), lane r's segment
-  // offset and chunk base, the x slice, and the slot metadata (lane j = slot j).
+  // All loads first: the chunk's rank bitmasks (one per lane), the row of the
+  // chunk's first token on rank lane, the x slice, and the slot metadata (lane
+  // j = slot j).
   const uint64_t lm_raw = a.token_ranks[min(tt, a.T - 1)];
-  const int seg = a.ws_rank_offsets[rl];
   const int cb = a.chunk_base[rl * a.NC + chunk];
   u32x4 v[U];
 #pragma unroll
@@ -180,7 +180,7 @@ __device__ __forceinline__ void dispatch_item(const DispatchArgs& a, int item, i
   const uint64_t mine = readlane64(lm, t & (kWave - 1)) & a.rank_bits;
   const int tl = t & (kWave - 1);
   const uint64_t lanes_below = tl == 0 ? 0ull : (~0ull >> (kWave - tl));
-  const int chunk_row = lane < a.R ? seg + cb : 0;  // lane r < R: first receive row of this chunk on rank r
+  const int chunk_row = lane < a.R ? cb : 0;  // lane r < R: first receive row of this chunk on rank r
 #pragma unroll
   for (int u = 0; u < U; ++u)
     if (c0 + u * kWave >= a.H8) v[u] = u32x4{0u, 0u, 0u, 0u};

@@ -1,16 +1,20 @@
 // Dispatch layout kernels: top-k expert ids -> is_token_in_rank, per-rank and
-// per-expert token counts, and the dispatch plan (per-token rank bitmask and
-// per-64-token-chunk exclusive prefix counts per rank).
+// per-expert token counts, and the dispatch plan: each token's rank bitmask
+// and, per rank and 64-token chunk, the receive row of the chunk's first token
+// going to that rank (segment offset plus the tokens of earlier chunks).
 //
 // Follows the is_token_in_rank filter of "DeepEP：年度总结中的计算通信重叠摘记"
 // (notes.kuangjux.top), section 节点内通信: a token is marked only for the
 // ranks that own one of its top-k experts.
 //
 // One lane per token, one wave per 64-token chunk.  Per-rank chunk counts come
-// from wave ballots (one ballot + popcount per rank), expert counts from an
-// LDS histogram; all counting is integer, so results do not depend on
-// scheduling.  Inter-block prefix sums are done by a second, single-block
-// kernel rather than by blocks waiting on each other.
+// from LDS atomics on the set rank bits, expert counts from an LDS histogram;
+// all counting is integer, so results do not depend on scheduling.  Up to 1024
+// tokens one block does everything.  Above, count blocks run in parallel and
+// add their rank and expert totals to accumulators in the workspace; the block
+// that finishes last ("last block done": every block takes a ticket from a
+// counter in the workspace) turns the chunk counts into receive rows and
+// resets the counter and the accumulators.  No block ever waits for another.
 #pragma once
 
 #include "device_common.h"
@@ -23,20 +27,35 @@ namespace moe {
 constexpr int kLayoutBlock = MOE_LAYOUT_BLOCK;  // tokens per block, multi-block path
 constexpr int kFusedMaxTokens = 1024;  // up to this many tokens one block does everything
 constexpr int kFusedMaxChunks = kFusedMaxTokens / kWave;
+constexpr int kCountTile = 4096;  // chunk counts staged in LDS per pass of the finalisation
+
+// Words at the start of the workspace that coordinate the blocks of one launch.
+// They are zero between calls: the caller zero-fills a new workspace once, and
+// every launch that uses them leaves them zero again.
+struct SyncWords {
+  uint32_t ticket;  // count blocks finished (last-block-done)
+  uint32_t role;    // role tickets taken (producers + dispatch in one launch)
+  uint32_t ready;   // 1 once the plan of the launch is complete
+  uint32_t exits;   // blocks of the launch that have finished with the sync words
+};
+constexpr int kSyncBytes = 256;
 
 struct LayoutArgs {
+  SyncWords* sync;
+  int32_t* expert_acc;      // [E] expert counts summed across blocks (zero between calls)
+  int32_t* rank_acc;        // [R] tokens per rank summed across blocks (zero between calls)
   const int32_t* topk_idx;
   int32_t* tokens_per_rank;
   int32_t* tokens_per_expert;
-  uint8_t* mask;           // [T, R] bytes
-  uint64_t* token_ranks;   // plan: [T] rank bitmask
-  int32_t* chunk_base;     // plan: [R, NC] chunk counts, then exclusive prefix per rank
-  int32_t* block_expert;   // plan scratch: [NB, E] per-block expert histogram
-  int32_t* ws_rank_offsets;// plan: [R + 1]
+  uint8_t* mask;            // [T, R] bytes
+  uint64_t* token_ranks;    // plan: [T] rank bitmask
+  int32_t* chunk_base;      // plan: [R, NC] receive row of the chunk's first token on rank r
+                            // (per-chunk counts while the count blocks run)
+  int32_t* ws_rank_offsets; // plan: [R + 1]
   uint64_t rank_magic;
   int T, k, E, R, NC, NB;
-  int mask_words;          // 1: mask rows written as 32-bit words (R % 4 == 0, aligned)
-  int ids_vec4;            // 1: id rows read as 16-byte vectors (k % 4 == 0, 16-byte aligned)
+  int mask_words;           // 1: mask rows written as 32-bit words (R % 4 == 0, aligned)
+  int ids_vec4;             // 1: id rows read as 16-byte vectors (k % 4 == 0, 16-byte aligned)
 };
 
 // Rank bitmask of token t; valid expert ids are added to the LDS histogram.
@@ -108,24 +127,51 @@ __device__ __forceinline__ int wave_rank_counts(uint64_t m, int R, int lane, int
   return lane < R ? cnt[lane] : 0;
 }
 
-// Wave 0: per-rank totals -> tokens_per_rank and the exclusive rank offsets.
-__device__ __forceinline__ void publish_rank_offsets(const LayoutArgs& a, const int* total, int lane) {
-  const int v = lane < a.R ? total[lane] : 0;
+// Wave 0: per-rank totals (lane r: total of rank r) -> tokens_per_rank and the
+// exclusive rank offsets; returns lane r's offset.
+__device__ __forceinline__ int publish_rank_offsets(const LayoutArgs& a, int v, int lane) {
+  v = lane < a.R ? v : 0;
   const int incl = wave_inclusive_scan(v, lane);
   if (lane < a.R) {
     a.tokens_per_rank[lane] = v;
     a.ws_rank_offsets[lane] = incl - v;
   }
   if (lane == a.R - 1) a.ws_rank_offsets[a.R] = incl;
+  return incl - v;
+}
+
+// Receive rows of the chunks of a batch of at most kFusedMaxTokens tokens, by
+// one block: cnt[c][r] holds the chunk counts (LDS); lanes r < R of wave 0
+// compute the rank totals, the offsets (published; offs[r], and offs[64] = the
+// number of receive rows) and the row of each chunk's first token.  offs: 65
+// ints of LDS.  Every thread of the block must call it.
+__device__ __forceinline__ void small_chunk_rows(const LayoutArgs& a, const int (*cnt)[kWave], int* offs) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  if (tid < kWave) {
+    int total = 0;
+    for (int c = 0; c < a.NC; ++c) total += cnt[c][lane];
+    const int off = publish_rank_offsets(a, total, lane);
+    offs[lane] = off;
+    if (lane == a.R - 1) offs[kWave] = off + total;
+  }
+  __syncthreads();
+  if (tid < a.R) {  // at most 16 chunks: a serial scan per rank is shortest
+    int run = offs[tid];
+    for (int c = 0; c < a.NC; ++c) {
+      put_coherent(&a.chunk_base[tid * a.NC + c], run);
+      run += cnt[c][tid];
+    }
+  }
 }
 
 // The whole layout in one block of at least ceil(T/64) waves (at most 16):
 // thread i owns token i, wave w chunk w; waves beyond the last chunk count
-// nothing.  hist: E ints of LDS.  Returns after wave 0 has published the rank
-// offsets; rank_total then holds the per-rank token counts.
+// nothing.  hist: E ints of LDS.  Returns (in every thread) once the plan is
+// written; offs[r] then holds the segment offset of rank r and offs[64] the
+// number of receive rows.
 template <int KI>
-__device__ __forceinline__ void layout_one_block(const LayoutArgs& a, int* hist, int* chunk_cnt,
-                                                 int (*wave_cnt)[kWave], int* rank_total) {
+__device__ __forceinline__ void layout_one_block(const LayoutArgs& a, int* hist, int (*cnt)[kWave],
+                                                 int (*wave_cnt)[kWave], int* offs) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   for (int e = tid; e < a.E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
@@ -135,40 +181,119 @@ __device__ __forceinline__ void layout_one_block(const LayoutArgs& a, int* hist,
     a.token_ranks[tid] = m;
     write_mask_row(a, tid, m);
   }
-  const int cnt = wave_rank_counts(m, a.R, lane, wave_cnt[wave]);
-  if (lane < a.R) chunk_cnt[lane * kFusedMaxChunks + wave] = cnt;
+  cnt[wave][lane] = wave_rank_counts(m, a.R, lane, wave_cnt[wave]);
   __syncthreads();
 
   for (int e = tid; e < a.E; e += blockDim.x) a.tokens_per_expert[e] = hist[e];
-  if (tid < a.R) {  // at most 16 chunks: a serial scan per rank is shortest
-    int run = 0;
-    for (int c = 0; c < a.NC; ++c) {
-      a.chunk_base[tid * a.NC + c] = run;
-      run += chunk_cnt[tid * kFusedMaxChunks + c];
-    }
-    rank_total[tid] = run;
-  }
+  small_chunk_rows(a, cnt, offs);
   __syncthreads();
-  if (wave == 0) publish_rank_offsets(a, rank_total, lane);
 }
 
 // T <= kFusedMaxTokens: one block of ceil(T/64) waves (at least one) does
-// everything in one launch.  Dynamic LDS: hist[E]; static: chunk counts [R][16].
+// everything in one launch.  Dynamic LDS: hist[E].
 template <int KI>
 __global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArgs a) {
   extern __shared__ int hist[];
-  __shared__ int chunk_cnt[kWave * kFusedMaxChunks];
+  __shared__ int cnt[kFusedMaxChunks][kWave];
   __shared__ int wave_cnt[kFusedMaxChunks][kWave];
-  __shared__ int rank_total[kWave];
-  layout_one_block<KI>(a, hist, chunk_cnt, wave_cnt, rank_total);
+  __shared__ int offs[kWave + 1];
+  layout_one_block<KI>(a, hist, cnt, wave_cnt, offs);
 }
 
-// Multi-block path, pass 1: mask rows, token bitmasks, chunk counts, block histograms.
+// Last-block-done.  Every wave of the block, having written with put_coherent
+// (or agent-scope atomics) everything the last block will read, waits for those
+// writes to complete; then one thread takes a ticket.  Returns true, in every
+// thread, in the block that drew the last of `blocks` tickets: every other
+// block's hand-off writes completed before its ticket was taken, so that block
+// reads them with get_coherent.  No thread waits for another block.
+__device__ __forceinline__ bool last_block_done(uint32_t* ticket, uint32_t blocks) {
+  __shared__ uint32_t drawn;
+  wait_own_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) drawn = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return drawn == blocks - 1;
+}
+
+// Resets a sync word for the next launch (all tickets of this one are taken).
+__device__ __forceinline__ void clear_word(uint32_t* w) { put_coherent(w, 0u); }
+
+// kBatch chunk counts of a tile (rank-major: element i = rank i / nc, chunk
+// c0 + i % nc) for element i0 + u * stride, u < kBatch, from clamped addresses,
+// all issued before any is used.
+template <int kBatch>
+__device__ __forceinline__ void load_count_batch(const LayoutArgs& a, int (&v)[kBatch], int i0, int stride, int n,
+                                                 int nc, int c0) {
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int i = min(i0 + u * stride, n - 1);
+    v[u] = get_coherent(&a.chunk_base[(i / nc) * a.NC + c0 + i % nc]);
+  }
+}
+
+// Plan finalisation of the multi-block paths, by the block that finished last
+// (any number of waves): rank offsets from the rank accumulator, expert totals
+// from the expert accumulator (both cleared for the next call), then the chunk
+// counts, kCountTile at a time, staged in LDS (tile), scanned per rank (one
+// wave per rank) and written back as receive rows.  The rank totals, the first
+// expert totals and the first batch of chunk counts are loaded together, so
+// shapes whose counts fit one batch take one round of loads.  offs: 64 ints of
+// LDS.  Every thread of the block must call it.
+__device__ __forceinline__ void finalize_chunk_rows(const LayoutArgs& a, int* tile, int* offs) {
+  constexpr int kBatch = 16;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int nthreads = blockDim.x, nwaves = nthreads >> 6;
+  const int TC = kCountTile / a.R;  // chunks of every rank per tile (R <= 64: at least 64)
+
+  const int rv = get_coherent(&a.rank_acc[min(lane, a.R - 1)]);
+  const int ev = get_coherent(&a.expert_acc[min(tid, a.E - 1)]);
+  int v[kBatch];
+  load_count_batch<kBatch>(a, v, tid, nthreads, a.R * min(TC, a.NC), min(TC, a.NC), 0);
+
+  if (wave == 0) {
+    offs[lane] = publish_rank_offsets(a, rv, lane);
+    if (lane < a.R) put_coherent(&a.rank_acc[lane], 0);
+  }
+  for (int e = tid; e < a.E; e += nthreads) {
+    a.tokens_per_expert[e] = e == tid ? ev : get_coherent(&a.expert_acc[e]);
+    put_coherent(&a.expert_acc[e], 0);
+  }
+  for (int c0 = 0; c0 < a.NC; c0 += TC) {
+    const int nc = min(TC, a.NC - c0), n = a.R * nc;
+    for (int i0 = tid; i0 < n; i0 += kBatch * nthreads) {
+      if (c0 != 0 || i0 != tid) load_count_batch<kBatch>(a, v, i0, nthreads, n, nc, c0);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (i0 + u * nthreads < n) tile[i0 + u * nthreads] = v[u];
+    }
+    __syncthreads();
+    for (int r = wave; r < a.R; r += nwaves) {
+      int run = offs[r];
+      for (int j0 = 0; j0 < nc; j0 += kWave) {
+        const int j = j0 + lane;
+        const int c = j < nc ? tile[r * nc + j] : 0;
+        const int incl = wave_inclusive_scan(c, lane);
+        if (j < nc) put_coherent(&a.chunk_base[r * a.NC + c0 + j], run + incl - c);
+        run += __builtin_amdgcn_readlane(incl, kWave - 1);
+      }
+      if (lane == 0) offs[r] = run;
+    }
+    __syncthreads();
+  }
+}
+
+// Multi-block path (T > kFusedMaxTokens), one launch: block b counts tokens
+// [256 b, 256 b + 256) -- mask rows, token bitmasks, the counts of its four
+// chunks, rank and expert totals added to the accumulators -- and the block that
+// finishes last turns the counts into receive rows.  Dynamic LDS: hist[E].
 template <int KI>
 __global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a) {
+  constexpr int kChunks = kLayoutBlock / kWave;
   extern __shared__ int hist[];  // [E]
-  __shared__ int wave_cnt[kLayoutBlock / kWave][kWave];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  __shared__ int wave_cnt[kChunks][kWave];
+  __shared__ int tile[kCountTile];
+  __shared__ int offs[kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   for (int e = tid; e < a.E; e += kLayoutBlock) hist[e] = 0;
   __syncthreads();
 
@@ -178,54 +303,19 @@ __global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a
     a.token_ranks[t] = m;
     write_mask_row(a, t, m);
   }
-  const int chunk = t >> 6;
-  const int cnt = wave_rank_counts(m, a.R, lane, wave_cnt[tid >> 6]);
-  if (chunk < a.NC && lane < a.R) a.chunk_base[lane * a.NC + chunk] = cnt;
+  const int cnt = wave_rank_counts(m, a.R, lane, wave_cnt[wave]);
+  const int chunk = blockIdx.x * kChunks + wave;
+  if (chunk < a.NC && lane < a.R) {
+    put_coherent(&a.chunk_base[lane * a.NC + chunk], cnt);
+    if (cnt) atomicAdd(&a.rank_acc[lane], cnt);
+  }
   __syncthreads();
-  for (int e = tid; e < a.E; e += kLayoutBlock) a.block_expert[(size_t)blockIdx.x * a.E + e] = hist[e];
-}
+  for (int e = tid; e < a.E; e += kLayoutBlock)
+    if (hist[e]) atomicAdd(&a.expert_acc[e], hist[e]);
 
-// Multi-block path, pass 2 (one block): expert totals, per-rank chunk prefix, rank offsets.
-__global__ __launch_bounds__(1024) void layout_finalize_kernel(LayoutArgs a) {
-  __shared__ int rank_total[kWave];
-  __shared__ int part_sum[1024];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int nwaves = blockDim.x >> 6;
-  // Expert totals: with E < blockDim, P = blockDim / E threads per expert each
-  // sum every P-th block row (independent loads, many in flight), then one
-  // thread adds the P partials.  Integer sums: the order does not matter.
-  const int P = a.E >= (int)blockDim.x ? 1 : (int)blockDim.x / a.E;
-  for (int i = tid; i < P * a.E; i += blockDim.x) {
-    const int e = i % a.E, part = i / a.E;
-    int s = 0;
-#pragma unroll 8
-    for (int b = part; b < a.NB; b += P) s += a.block_expert[(size_t)b * a.E + e];
-    if (P == 1)
-      a.tokens_per_expert[e] = s;
-    else
-      part_sum[i] = s;
-  }
-  for (int r = wave; r < a.R; r += nwaves) {
-    int* row = a.chunk_base + (size_t)r * a.NC;
-    int carry = 0;
-    for (int c0 = 0; c0 < a.NC; c0 += kWave) {
-      const int c = c0 + lane;
-      const int v = c < a.NC ? row[c] : 0;
-      const int incl = wave_inclusive_scan(v, lane);
-      if (c < a.NC) row[c] = carry + incl - v;
-      carry += __builtin_amdgcn_readlane(incl, kWave - 1);
-    }
-    if (lane == 0) rank_total[r] = carry;
-  }
-  __syncthreads();
-  if (P > 1) {
-    for (int e = tid; e < a.E; e += blockDim.x) {
-      int s = 0;
-      for (int q = 0; q < P; ++q) s += part_sum[q * a.E + e];
-      a.tokens_per_expert[e] = s;
-    }
-  }
-  if (wave == 0) publish_rank_offsets(a, rank_total, lane);
+  if (!last_block_done(&a.sync->ticket, gridDim.x)) return;
+  finalize_chunk_rows(a, tile, offs);
+  if (tid == 0) clear_word(&a.sync->ticket);
 }
 
 }  // namespace moe

@@ -34,7 +34,7 @@ constexpr int kMaxCuMaskWords = 32;  // up to 1024 compute units
 constexpr long kMinFp8Waves = 4096;
 
 struct PlanLayout {
-  size_t token_ranks, chunk_base, block_expert, rank_offsets, total;
+  size_t sync, expert_acc, rank_acc, token_ranks, chunk_base, rank_offsets, total;
   int NC, NB;
 };
 
@@ -59,12 +59,16 @@ PlanLayout plan_layout(const moe_shape& s) {
   p.NC = (int)((T + moe::kWave - 1) / moe::kWave);
   p.NB = (int)((T + moe::kLayoutBlock - 1) / moe::kLayoutBlock);
   size_t off = 0;
+  p.sync = off;  // sync words and the two accumulators: zero between calls
+  off = align_up(off + moe::kSyncBytes, kPlanAlign);
+  p.expert_acc = off;
+  off = align_up(off + E * sizeof(int32_t), kPlanAlign);
+  p.rank_acc = off;
+  off = align_up(off + R * sizeof(int32_t), kPlanAlign);
   p.token_ranks = off;
   off = align_up(off + T * sizeof(uint64_t), kPlanAlign);
   p.chunk_base = off;
   off = align_up(off + R * (size_t)p.NC * sizeof(int32_t), kPlanAlign);
-  p.block_expert = off;  // one histogram row per 64-token chunk (router path); NB <= NC
-  off = align_up(off + (size_t)std::max(p.NC, p.NB) * E * sizeof(int32_t), kPlanAlign);
   p.rank_offsets = off;
   off = align_up(off + (R + 1) * sizeof(int32_t), kPlanAlign);
   p.total = off;
@@ -267,22 +271,18 @@ void launch_ll_dispatch(int U, dim3 grid, hipStream_t stream, const moe::LlDispa
 }
 
 
+// One launch at every size; the routing block that finishes last finalises the plan.
 template <int P, int KS>
 void launch_router(int T, size_t lds, hipStream_t stream, const moe::RouterArgs& a) {
-  if (T <= moe::kFusedMaxTokens) {  // many one-wave blocks, then the one-block layout on the ids
-    if (T > 0) {
-      constexpr int tokens_per_wave = moe::kWave / P;
-      const int blocks = (T + tokens_per_wave - 1) / tokens_per_wave;
-      hipLaunchKernelGGL((moe::router_tokens_kernel<P, KS>), dim3(blocks), dim3(moe::kWave), 0, stream, a);
-    }
-    const int threads = std::max(moe::kWave, (T + moe::kWave - 1) / moe::kWave * moe::kWave);
-    if (a.lay.k <= 8)
-      hipLaunchKernelGGL(moe::layout_fused_kernel<8>, dim3(1), dim3(threads), lds, stream, a.lay);
-    else
-      hipLaunchKernelGGL(moe::layout_fused_kernel<moe::kMaxTopk>, dim3(1), dim3(threads), lds, stream, a.lay);
+  if (T == 0) {  // no tokens: one block writes zero counts and offsets
+    hipLaunchKernelGGL(moe::layout_fused_kernel<8>, dim3(1), dim3(moe::kWave), lds, stream, a.lay);
+  } else if (T <= moe::kFusedMaxTokens) {  // small blocks spread the routing over many CUs
+    constexpr int tokens_per_block = moe::kRouterSmallWaves * moe::kWave / P;
+    const int blocks = (T + tokens_per_block - 1) / tokens_per_block;
+    hipLaunchKernelGGL((moe::router_small_kernel<P, KS>), dim3(blocks), dim3(moe::kRouterSmallWaves * moe::kWave), 0,
+                       stream, a);
   } else {
     hipLaunchKernelGGL((moe::router_count_kernel<P, KS>), dim3(a.lay.NC), dim3(moe::kWave * P), lds, stream, a);
-    hipLaunchKernelGGL(moe::layout_finalize_kernel, dim3(1), dim3(1024), 0, stream, a.lay);
   }
 }
 
@@ -302,13 +302,15 @@ moe_status layout_args(const moe_shape& s, const int32_t* topk_idx, int32_t* tok
 
   char* ws = static_cast<char*>(workspace);
   a = moe::LayoutArgs{};
+  a.sync = reinterpret_cast<moe::SyncWords*>(ws + p.sync);
+  a.expert_acc = reinterpret_cast<int32_t*>(ws + p.expert_acc);
+  a.rank_acc = reinterpret_cast<int32_t*>(ws + p.rank_acc);
   a.topk_idx = topk_idx;
   a.tokens_per_rank = tokens_per_rank;
   a.tokens_per_expert = tokens_per_expert;
   a.mask = is_token_in_rank;
   a.token_ranks = reinterpret_cast<uint64_t*>(ws + p.token_ranks);
   a.chunk_base = reinterpret_cast<int32_t*>(ws + p.chunk_base);
-  a.block_expert = reinterpret_cast<int32_t*>(ws + p.block_expert);
   a.ws_rank_offsets = reinterpret_cast<int32_t*>(ws + p.rank_offsets);
   a.rank_magic = rank_magic(s);
   a.T = s.num_tokens;
@@ -331,13 +333,12 @@ void launch_layout(const moe::LayoutArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(moe::layout_fused_kernel<8>, dim3(1), dim3(threads), hist_bytes, stream, a);
     else
       hipLaunchKernelGGL(moe::layout_fused_kernel<moe::kMaxTopk>, dim3(1), dim3(threads), hist_bytes, stream, a);
-  } else {
+  } else {  // one launch: the count block that finishes last finalises the plan
     if (narrow)
       hipLaunchKernelGGL(moe::layout_count_kernel<8>, dim3(a.NB), dim3(moe::kLayoutBlock), hist_bytes, stream, a);
     else
       hipLaunchKernelGGL(moe::layout_count_kernel<moe::kMaxTopk>, dim3(a.NB), dim3(moe::kLayoutBlock), hist_bytes,
                          stream, a);
-    hipLaunchKernelGGL(moe::layout_finalize_kernel, dim3(1), dim3(1024), 0, stream, a);
   }
 }
 
@@ -514,6 +515,9 @@ moe_status moe_route_layout(const moe_shape* shape, const moe_router* router, co
 
   char* ws = static_cast<char*>(workspace);
   moe::RouterArgs a{};
+  a.lay.sync = reinterpret_cast<moe::SyncWords*>(ws + p.sync);
+  a.lay.expert_acc = reinterpret_cast<int32_t*>(ws + p.expert_acc);
+  a.lay.rank_acc = reinterpret_cast<int32_t*>(ws + p.rank_acc);
   a.logits = logits;
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
@@ -523,7 +527,6 @@ moe_status moe_route_layout(const moe_shape* shape, const moe_router* router, co
   a.lay.mask = is_token_in_rank;
   a.lay.token_ranks = reinterpret_cast<uint64_t*>(ws + p.token_ranks);
   a.lay.chunk_base = reinterpret_cast<int32_t*>(ws + p.chunk_base);
-  a.lay.block_expert = reinterpret_cast<int32_t*>(ws + p.block_expert);
   a.lay.ws_rank_offsets = reinterpret_cast<int32_t*>(ws + p.rank_offsets);
   a.lay.rank_magic = rank_magic(s);
   a.lay.T = s.num_tokens;
@@ -531,7 +534,7 @@ moe_status moe_route_layout(const moe_shape* shape, const moe_router* router, co
   a.lay.E = E;
   a.lay.R = s.num_ranks;
   a.lay.NC = p.NC;
-  a.lay.NB = p.NC;  // one expert histogram row per routed 64-token chunk
+  a.lay.NB = p.NC;  // one routing block per 64-token chunk
   a.lay.mask_words = (s.num_ranks % 4 == 0 && aligned(is_token_in_rank, 4)) ? 1 : 0;
   a.lay.ids_vec4 = (k % 4 == 0 && aligned(topk_idx, 16)) ? 1 : 0;  // the layout kernel's reads of the ids
   a.V = E % 16 == 0 ? E / 16 : E / 8;  // experts per lane: 16 or 8 lanes per token

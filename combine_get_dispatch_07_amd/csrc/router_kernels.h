@@ -11,10 +11,13 @@
 //   * weights: softmax over the k selected logits, or the sigmoid gate
 //     normalised over the k selected (fp32, expf);
 // and what the layout kernels compute from the ids: the token's rank bitmask
-// and is_token_in_rank row, per-64-token-chunk rank counts and per-chunk expert
-// histograms (router_count_kernel; layout_finalize_kernel follows).  For small
-// batches the router runs on one wave per 64 / P tokens to spread over many
-// CUs and layout_fused_kernel follows (router_tokens_kernel).
+// and is_token_in_rank row, per-64-token-chunk rank counts and expert counts.
+// One launch at every batch size: the routing block that finishes last
+// completes the plan (prefix sums, offsets, totals), so no host step or second
+// launch separates routing from the layout.  Batches above 1024 tokens route
+// one 64-token chunk per block (router_count_kernel); smaller ones use 4-wave
+// blocks of 16 or 32 tokens to spread the routing over more CUs
+// (router_small_kernel).
 //
 // Work split: P lanes per token (16 when E % 16 == 0, else 8), lane p
 // holding experts [p*V, p*V + V), V = E / P.  Candidates are ordered by (logit key, then lower expert id).
@@ -32,6 +35,7 @@
 namespace moe {
 
 constexpr int kRouterList = 4;  // KL: list entries per lane
+constexpr int kRouterSmallWaves = 4;  // waves per block of router_small_kernel
 constexpr int kRouterMaxK = 16;  // slots per token handled (one or two per lane)
 
 struct RouterArgs {
@@ -263,14 +267,35 @@ __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int 
   return live ? ranks : 0;
 }
 
+// Writes token t's rank bitmask (lane p == 0 of its P lanes) and its
+// is_token_in_rank row (spread over the P lanes).
+template <int P, bool kBitmask = true>
+__device__ __forceinline__ void write_token_layout(const LayoutArgs& L, int t, int p, uint64_t m) {
+  if (t >= L.T) return;
+  if (kBitmask && p == 0) L.token_ranks[t] = m;
+  uint8_t* dst = L.mask + (size_t)t * L.R;
+  if (L.mask_words) {
+    uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+    for (int w = p; w < (L.R >> 2); w += P) {
+      const uint32_t b = (uint32_t)(m >> (4 * w)) & 0xfu;
+      d32[w] = (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
+    }
+  } else {
+    for (int r = p; r < L.R; r += P) dst[r] = (uint8_t)((m >> r) & 1u);
+  }
+}
+
 // T > kFusedMaxTokens (so T >= 1): block b routes chunk b (64 tokens, 64 / P
-// per wave) and writes everything layout_count_kernel writes for it (rank
-// bitmasks, mask rows, chunk counts, an expert histogram row);
-// layout_finalize_kernel (with NB = number of chunks) completes the layout.
+// per wave) and writes what layout_count_kernel writes for it (rank bitmasks,
+// mask rows, the chunk's counts, rank and expert totals added to the
+// accumulators); the block that finishes last turns the counts into receive
+// rows.  Dynamic LDS: hist[E].
 template <int P, int KS>
 __global__ __launch_bounds__(kWave * P) void router_count_kernel(RouterArgs a) {
   extern __shared__ int hist[];  // [E]
   __shared__ int chunk_cnt[kWave];  // per-rank token counts of this chunk
+  __shared__ int tile[kCountTile];
+  __shared__ int offs[kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const LayoutArgs& L = a.lay;
   for (int e = tid; e < L.E; e += kWave * P) hist[e] = 0;
@@ -285,33 +310,75 @@ __global__ __launch_bounds__(kWave * P) void router_count_kernel(RouterArgs a) {
 #pragma unroll
   for (int q = 0; q < KS; ++q)
     if (sel[q] >= 0) atomicAdd(&hist[sel[q]], 1);
-  if (t < L.T) {
-    if (p == 0) L.token_ranks[t] = m;
-    uint8_t* dst = L.mask + (size_t)t * L.R;
-    if (L.mask_words) {
-      uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
-      for (int w = p; w < (L.R >> 2); w += P) {
-        const uint32_t b = (uint32_t)(m >> (4 * w)) & 0xfu;
-        d32[w] = (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
-      }
-    } else {
-      for (int r = p; r < L.R; r += P) dst[r] = (uint8_t)((m >> r) & 1u);
-    }
-  }
+  write_token_layout<P>(L, t, p, m);
   if (p == 0) add_rank_bits(m, chunk_cnt);
   __syncthreads();
 
-  if (tid < L.R) L.chunk_base[tid * L.NC + blockIdx.x] = chunk_cnt[tid];
-  for (int e = tid; e < L.E; e += kWave * P) L.block_expert[(size_t)blockIdx.x * L.E + e] = hist[e];
+  // what the last block reads: the chunk's counts and the totals
+  if (tid < L.R) {
+    const int c = chunk_cnt[tid];
+    put_coherent(&L.chunk_base[tid * L.NC + blockIdx.x], c);
+    if (c) atomicAdd(&L.rank_acc[tid], c);
+  }
+  for (int e = tid; e < L.E; e += kWave * P)
+    if (hist[e]) atomicAdd(&L.expert_acc[e], hist[e]);
+
+  if (!last_block_done(&L.sync->ticket, gridDim.x)) return;
+  finalize_chunk_rows(L, tile, offs);
+  if (tid == 0) clear_word(&L.sync->ticket);
 }
 
-// 1 <= T <= kFusedMaxTokens: one wave per 64 / P tokens, ids and weights
-// only; layout_fused_kernel follows on the ids.
+// Plan of a batch of at most kFusedMaxTokens tokens from the token bitmasks
+// handed over by the routing blocks, by one block of any number of waves:
+// per-chunk rank counts (one ballot per rank over the chunk's 64 tokens), rank
+// offsets and totals, the chunks' receive rows; tokens per expert from the
+// accumulator, which is cleared for the next call.  offs: 65 ints of LDS.
+__device__ __forceinline__ void finalize_small_plan(const LayoutArgs& a, int (*cnt)[kWave], int* offs) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int nthreads = blockDim.x, nwaves = nthreads >> 6;
+  for (int c = wave; c < a.NC; c += nwaves) {
+    const int t = c * kWave + lane;
+    const uint64_t m_raw = get_coherent(&a.token_ranks[min(t, a.T - 1)]);
+    const uint64_t m = t < a.T ? m_raw : 0ull;
+    int mine = 0;
+    for (int r = 0; r < a.R; ++r) {
+      const int n = __popcll(__ballot((m >> r) & 1ull));
+      mine = lane == r ? n : mine;
+    }
+    cnt[c][lane] = mine;
+  }
+  for (int e = tid; e < a.E; e += nthreads) {
+    a.tokens_per_expert[e] = get_coherent(&a.expert_acc[e]);
+    put_coherent(&a.expert_acc[e], 0);
+  }
+  __syncthreads();
+  small_chunk_rows(a, cnt, offs);
+}
+
+// 1 <= T <= kFusedMaxTokens: blocks of kRouterSmallWaves waves route
+// kRouterSmallWaves * 64 / P tokens each, write ids, weights, bitmasks (handed
+// to the last block) and mask rows, and add their expert counts to the
+// workspace accumulator; the block that finishes last computes the rest of the
+// plan.
 template <int P, int KS>
-__global__ __launch_bounds__(kWave) void router_tokens_kernel(RouterArgs a) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kRouterSmallWaves * kWave) void router_small_kernel(RouterArgs a) {
+  __shared__ int cnt[kFusedMaxChunks][kWave];
+  __shared__ int offs[kWave + 1];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const LayoutArgs& L = a.lay;
+  const int t = blockIdx.x * (kRouterSmallWaves * kWave / P) + tid / P;
+  const int p = lane & (P - 1);
   int sel[KS];
-  route_token<P, KS>(a, blockIdx.x * (kWave / P) + lane / P, lane, sel);
+  const uint64_t m = route_token<P, KS>(a, t, lane, sel);
+#pragma unroll
+  for (int q = 0; q < KS; ++q)
+    if (sel[q] >= 0) atomicAdd(&L.expert_acc[sel[q]], 1);
+  if (p == 0 && t < L.T) put_coherent(&L.token_ranks[t], m);
+  write_token_layout<P, false>(L, t, p, m);
+
+  if (!last_block_done(&L.sync->ticket, gridDim.x)) return;
+  finalize_small_plan(L, cnt, offs);
+  if (tid == 0) clear_word(&L.sync->ticket);
 }
 
 }  // namespace moe

@@ -37,9 +37,9 @@ template <int U, bool kFp8, int KI>
 __global__ __launch_bounds__(kSendSmallMaxWaves * kWave) void send_small_kernel(SendSmallArgs args) {
 #pragma clang fp contract(off)
   extern __shared__ int hist[];
-  __shared__ int chunk_cnt[kWave * kFusedMaxChunks];
+  __shared__ int chunk_cnt[kFusedMaxChunks][kWave];
   __shared__ int wave_cnt[kFusedMaxChunks][kWave];
-  __shared__ int rank_total[kWave];  // tokens per rank
+  __shared__ int rank_total[kWave + 1];  // layout block: offsets; token blocks: tokens per rank
   __shared__ int before[kWave];      // token blocks: tokens before t going to each rank
   const LayoutArgs& L = args.lay;
   const DispatchArgs& a = args.d;
@@ -49,12 +49,10 @@ __global__ __launch_bounds__(kSendSmallMaxWaves * kWave) void send_small_kernel(
   if (blockIdx.x == a.T) {  // the layout, then the dispatch's segment offsets and row count
     layout_one_block<KI>(L, hist, chunk_cnt, wave_cnt, rank_total);
     if (wave == 0) {
-      const int v = lane < a.R ? rank_total[lane] : 0;
-      const int incl = wave_inclusive_scan(v, lane);
-      if (lane < a.R) a.rank_offsets[lane] = incl - v;
-      if (lane == a.R - 1) {
-        a.rank_offsets[a.R] = incl;
-        *a.num_recv = incl;
+      if (lane < a.R) a.rank_offsets[lane] = rank_total[lane];
+      if (lane == 0) {
+        a.rank_offsets[a.R] = rank_total[kWave];
+        *a.num_recv = rank_total[kWave];
       }
     }
     return;

@@ -92,7 +92,12 @@ const char* moe_status_string(moe_status status);
 /* Bytes of device workspace the layout writes and dispatch reads for `shape`
  * (0 if the shape is invalid).  The workspace is the dispatch plan: the
  * per-token rank bitmasks, per-64-token-chunk prefix counts per rank and the
- * rank offsets.  It carries no state across different layouts. */
+ * rank offsets.  Its first bytes also hold words through which the blocks of
+ * one launch hand the plan's last step to the block that finishes last:
+ * ZERO-FILL A NEW WORKSPACE ONCE before its first use (hipMemset); every call
+ * leaves those words zero again, so a workspace is reused without clearing.
+ * Calls sharing a workspace must not run concurrently (they already share the
+ * plan).  The plan carries no state across different layouts. */
 size_t moe_workspace_bytes(const moe_shape* shape);
 
 /* Worst-case receive rows, T * min(k, R): every token sent to min(k, R)
@@ -107,7 +112,12 @@ int32_t moe_max_recv_rows(const moe_shape* shape);
  *   tokens_per_expert out int32[E]      number of valid slots naming each expert
  *   is_token_in_rank  out uint8[T, R]   1 iff a valid slot of token t names an expert of rank r, else 0
  *   workspace         out bytes[ws]     dispatch plan consumed by moe_dispatch
- *                                       (workspace_bytes >= moe_workspace_bytes(shape))
+ *                                       (workspace_bytes >= moe_workspace_bytes(shape);
+ *                                       zero-filled once when allocated, see above)
+ *
+ * One launch at every size: up to 1024 tokens one block does everything; above,
+ * blocks of 256 tokens count in parallel and the block that finishes last takes
+ * the prefix sums (no block waits for another).
  */
 moe_status moe_get_dispatch_layout(const moe_shape* shape, const int32_t* topk_idx,
                                    int32_t* tokens_per_rank, int32_t* tokens_per_expert,

@@ -80,6 +80,7 @@ int main(void) {
   CHECK_HIP(hipMalloc((void**)&dtpe, E * sizeof(int32_t)));
   CHECK_HIP(hipMalloc((void**)&dmask, T * R));
   CHECK_HIP(hipMalloc(&dws, ws_bytes));
+  CHECK_HIP(hipMemset(dws, 0, ws_bytes)); /* a new workspace is zero-filled once */
   CHECK_HIP(hipMalloc((void**)&drecv, (size_t)cap * H * sizeof(uint16_t)));
   CHECK_HIP(hipMalloc((void**)&dsrc, cap * sizeof(int32_t)));
   CHECK_HIP(hipMalloc((void**)&dridx, (size_t)cap * K * sizeof(int32_t)));

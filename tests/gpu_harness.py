@@ -26,8 +26,10 @@ def bf16_to_np(t: torch.Tensor) -> np.ndarray:
 
 
 def _poison(d: Dict[str, Optional[torch.Tensor]]) -> None:
-    for v in d.values():
-        if v is not None:
+    """Fills every output with the poison byte; the workspace keeps its zero fill (the library
+    requires a zero-filled workspace before its first use)."""
+    for k, v in d.items():
+        if v is not None and k != "workspace":
             v.view(torch.uint8).fill_(POISON)
 
 
