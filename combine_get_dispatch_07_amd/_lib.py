@@ -88,6 +88,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_combine_ll.restype = ctypes.c_int
     lib.moe_layout_dispatch.argtypes = [SH, ctypes.c_int, P, P, P, P, P, P, P, SZ, I32, P, P, P, P, P, P, P, P, P]
     lib.moe_layout_dispatch.restype = ctypes.c_int
+    lib.moe_layout_dispatch_noalloc.argtypes = [SH, ctypes.c_int, P, P, P, P, P, P, I32, P, P, P, P, P, P, P, P, P]
+    lib.moe_layout_dispatch_noalloc.restype = ctypes.c_int
     lib.moe_encode_e4m3.argtypes = [P, P, ctypes.c_int64, P]
     lib.moe_encode_e4m3.restype = ctypes.c_int
     lib.moe_combine_backward.argtypes = [SH, P, P, I32, P, P, P, P, P, P]
@@ -232,6 +234,28 @@ def moe_layout_dispatch(shape: MoeShape, dtype: str, x, topk_idx, topk_w, tokens
         _ptr(tokens_per_expert, "tokens_per_expert", torch.int32, E),
         _ptr(is_token_in_rank, "is_token_in_rank", torch.uint8, T * R),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), cap,
+        _ptr(recv_x, "recv_x", torch.uint8 if fp8 else torch.bfloat16, cap * H),
+        _ptr(recv_scales, "recv_scales", torch.float32, cap * (H // 128)) if fp8 else None,
+        _ptr(recv_src_idx, "recv_src_idx", torch.int32, cap),
+        _ptr(recv_topk_idx, "recv_topk_idx", torch.int32, cap * k),
+        _ptr(recv_topk_w, "recv_topk_w", torch.float32, cap * k),
+        _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),
+        _ptr(send_row, "send_row", torch.int32, T * R), _ptr(num_recv, "num_recv", torch.int32, 1)), stream, prepare, locals())
+
+
+def moe_layout_dispatch_noalloc(shape: MoeShape, dtype: str, x, topk_idx, topk_w, tokens_per_rank,
+                                tokens_per_expert, is_token_in_rank, recv_x, recv_scales, recv_src_idx, recv_topk_idx,
+                                recv_topk_w, rank_offsets, send_row, num_recv, stream=None, prepare: bool = False):
+    """moe_layout_dispatch with the plan in the library's static device array (no workspace)."""
+    T, H, k, E, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts, shape.num_ranks
+    fp8 = DTYPES[dtype] == MOE_FP8_E4M3
+    cap = recv_src_idx.numel()
+    return _launch("moe_layout_dispatch_noalloc", (
+        ctypes.byref(shape.c()), DTYPES[dtype], _ptr(x, "x", torch.bfloat16, T * H),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
+        _ptr(tokens_per_rank, "tokens_per_rank", torch.int32, R),
+        _ptr(tokens_per_expert, "tokens_per_expert", torch.int32, E),
+        _ptr(is_token_in_rank, "is_token_in_rank", torch.uint8, T * R), cap,
         _ptr(recv_x, "recv_x", torch.uint8 if fp8 else torch.bfloat16, cap * H),
         _ptr(recv_scales, "recv_scales", torch.float32, cap * (H // 128)) if fp8 else None,
         _ptr(recv_src_idx, "recv_src_idx", torch.int32, cap),

@@ -449,6 +449,41 @@ bool launch_send_small(const moe::LayoutArgs& lay, const moe::DispatchArgs& d, b
   return true;
 }
 
+// Device memory of moe_layout_dispatch_noalloc: the plan (workspace) kept in a
+// file-scope array, for callers that cannot allocate.  Every device the library
+// runs on holds its own copy until the process ends.  Static device memory is
+// zero-filled when the code object is loaded, and every launch leaves the
+// plan's sync words and accumulators zero again, as a caller-allocated
+// workspace requires.  In host code the name `scratch` is only a host-side
+// stand-in: its device address comes from hipGetSymbolAddress, once per
+// device (scratch_ptr), and only that address is passed to kernels.
+constexpr size_t kScratchBytes = 4u << 20;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+// Address of this device's `scratch`, looked up on the first call on each
+// device; nullptr if the lookup fails.
+void* scratch_ptr() {
+  static std::atomic<void*> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = cached[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  cached[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -593,6 +628,34 @@ moe_status moe_layout_dispatch(const moe_shape* shape, moe_dtype dtype, const vo
     launch_dispatch_args(d, U, fp8, stream);
   }
   return last_launch_status();
+}
+
+moe_status moe_layout_dispatch_noalloc(const moe_shape* shape, moe_dtype dtype, const void* x,
+                                       const int32_t* topk_idx, const float* topk_w, int32_t* tokens_per_rank,
+                                       int32_t* tokens_per_expert, uint8_t* is_token_in_rank, int32_t recv_capacity,
+                                       void* recv_x, float* recv_scales, int32_t* recv_src_idx,
+                                       int32_t* recv_topk_idx, float* recv_topk_w, int32_t* rank_offsets,
+                                       int32_t* send_row, int32_t* num_recv, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (plan_layout(*shape).total > kScratchBytes) return MOE_ERR_UNSUPPORTED;
+  // every argument check of moe_layout_dispatch first (with a stand-in address
+  // if the array's address is unavailable), so errors are reported alike
+  void* ws = scratch_ptr();
+  void* ws_checked = ws != nullptr ? ws : reinterpret_cast<void*>(kPlanAlign);
+  moe::LayoutArgs lay;
+  st = layout_args(*shape, topk_idx, tokens_per_rank, tokens_per_expert, is_token_in_rank, ws_checked, kScratchBytes,
+                   lay);
+  if (st != MOE_OK) return st;
+  moe::DispatchArgs d;
+  int U = 1;
+  st = dispatch_args(*shape, dtype, x, topk_idx, topk_w, ws_checked, kScratchBytes, recv_capacity, recv_x,
+                     recv_scales, recv_src_idx, recv_topk_idx, recv_topk_w, rank_offsets, send_row, num_recv, d, U);
+  if (st != MOE_OK) return st;
+  if (ws == nullptr) return MOE_ERR_HIP;
+  return moe_layout_dispatch(shape, dtype, x, topk_idx, topk_w, tokens_per_rank, tokens_per_expert,
+                             is_token_in_rank, ws, kScratchBytes, recv_capacity, recv_x, recv_scales, recv_src_idx,
+                             recv_topk_idx, recv_topk_w, rank_offsets, send_row, num_recv, stream);
 }
 
 moe_status moe_combine(const moe_shape* shape, const void* y, int32_t num_y_rows,

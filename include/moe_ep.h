@@ -216,6 +216,25 @@ moe_status moe_layout_dispatch(const moe_shape* shape, moe_dtype dtype, const vo
                                int32_t* recv_topk_idx, float* recv_topk_w, int32_t* rank_offsets,
                                int32_t* send_row, int32_t* num_recv, hipStream_t stream);
 
+/* moe_layout_dispatch without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The dispatch plan lives in a static
+ * device array of the library, 4 MiB per device (held until the process
+ * ends); shapes whose plan (moe_workspace_bytes) exceeds 4 MiB are rejected
+ * with MOE_ERR_UNSUPPORTED -- about 300,000 tokens at 256 experts and 64
+ * ranks.  The call allocates nothing and otherwise behaves exactly as
+ * moe_layout_dispatch: same arguments (minus the workspace), outputs, limits
+ * and errors; MOE_ERR_HIP if the array's device address cannot be obtained.
+ * All calls on one device share the array: calls that overlap in time on one
+ * device (on different streams, or from several threads) race and give
+ * undefined results.  Each call leaves the array ready for the next. */
+moe_status moe_layout_dispatch_noalloc(const moe_shape* shape, moe_dtype dtype, const void* x,
+                                       const int32_t* topk_idx, const float* topk_w, int32_t* tokens_per_rank,
+                                       int32_t* tokens_per_expert, uint8_t* is_token_in_rank, int32_t recv_capacity,
+                                       void* recv_x, float* recv_scales, int32_t* recv_src_idx,
+                                       int32_t* recv_topk_idx, float* recv_topk_w, int32_t* rank_offsets,
+                                       int32_t* send_row, int32_t* num_recv, hipStream_t stream);
+
 /* The E4M3 rounding the FP8 dispatch applies to x / s, on its own.
  * [overlap notes, 节点内通信: FP8 transport.]
  *

@@ -191,6 +191,29 @@ def test_layout_dispatch_rejections():
     assert fn(None, 0, A, A, A, A, A, A, A, 1 << 30, cap, A, A, A, A, A, A, A, A, None) == INVALID
 
 
+def test_layout_dispatch_noalloc_rejections():
+    """The no-allocation variant checks what moe_layout_dispatch checks, and rejects shapes whose
+    plan does not fit its 4 MiB static array, before any launch."""
+    fn = L.lib.moe_layout_dispatch_noalloc
+    s = shape()
+    cap = s.num_tokens * min(s.num_topk, s.num_ranks)
+
+    def call(sh=s, dtype=0, cap_=cap, mask=A, x=A, scales=A):
+        return fn(ctypes.byref(sh), dtype, x, A, A, A, A, mask, cap_, A, scales, A, A, A, A, A, A, None)
+
+    assert call(dtype=7) == INVALID
+    assert call(cap_=cap - 1) == CAPACITY
+    assert call(mask=None) == INVALID
+    assert call(x=A + 2) == INVALID
+    assert call(dtype=1, scales=None) == INVALID
+    big = L.MoeShape(1 << 20, 256, 8, 256, 64).c()  # plan: 8 MiB of token bitmasks alone
+    assert L.lib.moe_workspace_bytes(ctypes.byref(big)) > 4 << 20
+    assert call(sh=big, cap_=(1 << 20) * 8) == UNSUPPORTED
+    ok = L.MoeShape(300000, 256, 8, 256, 64).c()  # the documented reach: about 300,000 tokens
+    assert L.lib.moe_workspace_bytes(ctypes.byref(ok)) <= 4 << 20
+    assert fn(None, 0, A, A, A, A, A, A, cap, A, A, A, A, A, A, A, A, None) == INVALID
+
+
 def test_prepared_call_checks_its_tensors_once_at_prepare_time():
     """prepare=True runs the wrapper's tensor checks up front (CPU tensors are refused) and
     converts the remaining integer arguments to the declared ctypes types."""
