@@ -451,19 +451,33 @@ def graph_us(torch, fn, reps: int = 20, repeats: int = 5) -> float:
 
 def router_timing(cfg, torch, moe, W, nsets: int = 8) -> dict:
     """Top-k gating fused with the layout against the layout alone on the same ids, and against a
-    plain torch gate (topk + softmax/sigmoid, no group limit) for context."""
+    plain torch gate (topk + softmax/sigmoid, no group limit) for context.  Also the whole send side
+    from logits: moe_route_dispatch (one kernel up to 1024 tokens) against moe_route_layout followed
+    by moe_dispatch."""
+    import numpy as np
     grouped = cfg.routing == "group_limited"
     gate = "sigmoid" if cfg.routing == "sigmoid" else "softmax"
     G, KG = (cfg.num_groups, cfg.topk_groups) if grouped else (1, 1)
     shape = moe.MoeShape(cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks)
     logits = torch.from_numpy(W.config_logits(cfg)).cuda()
+    x = torch.from_numpy(W.make_inputs(cfg)["x"].view(np.int16)).view(torch.bfloat16).cuda()
+    dtype = cfg.dispatch_dtype
     sets = []
     for _ in range(nsets):
         lay = moe.alloc_route(shape)
-        sets.append({"logits": logits.clone(), "lay": lay})
+        sets.append({"logits": logits.clone(), "lay": lay, "x": x.clone(), "d": moe.alloc_dispatch(shape, dtype)})
     for s in sets:
         moe.run_route(shape, s["logits"], s["lay"], gate, G, KG)
     torch.cuda.synchronize()
+
+    def route_dispatch(r):
+        s = sets[r % nsets]
+        moe.run_route_dispatch(shape, dtype, s["logits"], s["x"], s["lay"], s["d"], gate, G, KG)
+
+    def route_then_dispatch(r):
+        s = sets[r % nsets]
+        moe.run_route(shape, s["logits"], s["lay"], gate, G, KG)
+        moe.run_dispatch(shape, dtype, s["x"], s["lay"]["topk_idx"], s["lay"]["topk_w"], s["lay"], s["d"])
 
     def fused(r):
         s = sets[r % nsets]
@@ -486,7 +500,10 @@ def router_timing(cfg, torch, moe, W, nsets: int = 8) -> dict:
            "route_layout_us": round(graph_us(torch, fused), 2),
            "layout_only_us": round(graph_us(torch, layout_only), 2),
            "torch_topk_gate_us": round(graph_us(torch, torch_gate), 2),
-           "algorithmic_bytes": nbytes}
+           "algorithmic_bytes": nbytes,
+           "route_dispatch_one_call_us": round(graph_us(torch, route_dispatch), 2),
+           "route_then_dispatch_us": round(graph_us(torch, route_then_dispatch), 2),
+           "dispatch_dtype": dtype}
     out["route_layout_GB_per_s"] = round(nbytes / (out["route_layout_us"] * 1e-6) / 1e9, 1)
     return out
 
@@ -595,8 +612,22 @@ def _cpu_model() -> str:
     return "unknown cpu"
 
 
-def cpu_baseline(cfg, W, budget_s: float = 20.0) -> dict:
-    """The numpy oracle, as it stands, on the same workload (host cores)."""
+def _numpy_threads() -> dict:
+    """Threads the oracle's numpy can use: element-wise ufuncs run on the calling thread; the BLAS
+    pool (not used by the oracle) is reported for completeness."""
+    out = {"elementwise": 1}
+    try:
+        from threadpoolctl import threadpool_info
+        out["blas"] = sum(int(p.get("num_threads", 0)) for p in threadpool_info() if p.get("user_api") == "blas")
+    except Exception:  # threadpoolctl missing or unable to inspect: the element-wise figure stands
+        pass
+    return out
+
+
+def cpu_ops(cfg, W, repeats: int = 3) -> dict:
+    """The numpy oracle, as it stands, per op on the full workload: µs per call (median of `repeats`)
+    and GB/s with the GPU's algorithmic byte formulas.  layout = counts and mask; dispatch = receive
+    rows, their metadata and payload (bf16 copy or FP8 quantisation); combine = the weighted sum."""
     import numpy as np
 
     from oracle import moe_oracle as O
@@ -604,31 +635,63 @@ def cpu_baseline(cfg, W, budget_s: float = 20.0) -> dict:
     d = W.make_inputs(cfg)
     x, idx, w = d["x"], d["topk_idx"], d["topk_w"]
     E, R = cfg.num_experts, cfg.num_ranks
-    _, _, mask = O.get_dispatch_layout(idx, E, R)
-    y = W.draw_expert_outputs(W.y_stream(cfg), int(mask.sum()), cfg.hidden)
-    times, n = [], 0
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        ref = O.run_all(x, idx, w, E, R, cfg.dispatch_dtype)
-        O.combine(y, idx, w, ref["send_row"], E, R)
-        times.append(time.perf_counter() - t0)
-        n = int(ref["num_recv"])
-        if time.perf_counter() - t_start > budget_s / 2 or len(times) >= 5:
-            break
-    b = algorithmic_bytes(cfg, n)
-    step_bytes = b["layout"] + b["dispatch"] + b["combine"]
-    med = float(np.median(times))
-    return {
-        "value": round(step_bytes / med / 1e9, 3),
+    _, _, mask0 = O.get_dispatch_layout(idx, E, R)
+    y = W.draw_expert_outputs(W.y_stream(cfg), int(mask0.sum()), cfg.hidden)
+    state = {}
+
+    def layout():
+        state["mask"] = O.get_dispatch_layout(idx, E, R)[2]
+
+    def dispatch():
+        _, send_row, n = O.assign_slots(state["mask"])
+        src, _, _ = O.dispatch_metadata(idx, w, E, R, send_row, n)
+        if cfg.dispatch_dtype == "bf16":
+            O.dispatch_rows_bf16(x, src)
+        else:
+            O.dispatch_rows_fp8(x, src)
+        state["send_row"], state["n"] = send_row, n
+
+    def combine():
+        O.combine(y, idx, w, state["send_row"], E, R)
+
+    out = {}
+    for name, fn in (("layout", layout), ("dispatch", dispatch), ("combine", combine)):
+        times = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        out[name] = float(np.median(times))
+    b = algorithmic_bytes(cfg, state["n"])
+    return {op: {"us": round(out[op] * 1e6, 1), "GB_per_s": round(b[op] / out[op] / 1e9, 3)} for op in out}
+
+
+def cpu_baseline(cfg, W, secondary=None) -> dict:
+    """The numpy oracle timed on the host cores: per op on the main workload (and on `secondary`),
+    with `value` the whole step's algorithmic bytes over the summed per-op medians."""
+    ops = cpu_ops(cfg, W)
+    step_s = sum(op["us"] for op in ops.values()) * 1e-6
+    d = W.make_inputs(cfg)
+    from oracle import moe_oracle as O
+    _, _, mask = O.get_dispatch_layout(d["topk_idx"], cfg.num_experts, cfg.num_ranks)
+    b = algorithmic_bytes(cfg, int(mask.sum()))
+    threads = _numpy_threads()
+    out = {
+        "value": round((b["layout"] + b["dispatch"] + b["combine"]) / step_s / 1e9, 3),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"full {cfg.name} workload, layout+dispatch+combine, median of {len(times)} passes "
-                  f"({med:.2f} s each); numpy elementwise work runs on one core "
-                  f"(host: {_cpu_model()}, {os.cpu_count()} cpus, {len(os.sched_getaffinity(0))} in this "
-                  f"process's affinity)",
+        "sample": f"full {cfg.name} workload, layout, dispatch and combine each timed as the median of 3 "
+                  f"calls ({step_s:.2f} s per step); numpy element-wise work runs on one core",
+        "ops": ops,
+        "cpu_model": _cpu_model(),
+        "cpu_count": os.cpu_count(),
+        "affinity": len(os.sched_getaffinity(0)),
+        "numpy_threads": threads,
     }
+    if secondary is not None:
+        out["secondary"] = {"workload": secondary.name, "ops": cpu_ops(secondary, W)}
+    return out
 
 
 def copy_reference(torch, nbytes: int = 512 << 20, reps: int = 10) -> dict:
@@ -653,14 +716,15 @@ def copy_reference(torch, nbytes: int = 512 << 20, reps: int = 10) -> dict:
     return {"bytes_moved": 2 * nbytes, "us": round(us, 1), "GB_per_s": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
 
 
-HBM_CEILING = os.path.join(ROOT, "combine_get_dispatch_07_amd", "hbm_ceiling")
+HBM_CEILING = os.path.join(ROOT, "hbm_ceiling")
+LAUNCH_FLOOR = os.path.join(ROOT, "liblaunch_floor.so")
 # The probe's mix closest to each kernel's read/write mix
 CEILING_MIX = {"dispatch": "read1_write5", "combine": "read5_write1",
                "combine_backward": "read5_write5", "dispatch_backward": "read5_write1"}
 
 
 def hbm_ceiling():
-    """Best streaming bandwidth per read/write mix (csrc/hbm_ceiling.hip, built by build.py),
+    """Best streaming bandwidth per read/write mix (hbm_ceiling.hip, built by build.py),
     or None when the probe is not built."""
     import subprocess
 
@@ -671,6 +735,38 @@ def hbm_ceiling():
     if res.returncode != 0:
         raise RuntimeError(f"hbm_ceiling failed ({res.returncode}): {res.stderr.strip()}")
     return json.loads(res.stdout)
+
+
+def launch_floor(torch) -> dict:
+    """The shortest launches (launch_floor.hip, built by build.py), timed like the ops' us_kernel:
+    graphs of back-to-back launches.  `empty_us`: a one-wave kernel that does nothing;
+    `load_store_us`: a one-wave kernel whose lane 0 loads one 16-byte value and stores it, the
+    launches of a graph reading 64 addresses 16 MiB apart (1 GiB in all) so that consecutive
+    launches touch different lines.  None when the probe is not built."""
+    import ctypes
+
+    if not os.path.exists(LAUNCH_FLOOR):
+        log("launch_floor is not built; skipping the launch floor")
+        return None
+    lib = ctypes.CDLL(LAUNCH_FLOOR)
+    lib.floor_empty.argtypes = [ctypes.c_void_p]
+    lib.floor_load_store.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(64 * 16, dtype=torch.uint8, device="cuda")
+    srcs = [src.data_ptr() + r * (16 << 20) for r in range(64)]
+    dsts = [dst.data_ptr() + 16 * r for r in range(64)]
+
+    def empty(r):
+        if lib.floor_empty(torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("floor_empty launch failed")
+
+    def load_store(r):
+        if lib.floor_load_store(srcs[r % 64], dsts[r % 64], torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("floor_load_store launch failed")
+
+    out = {"empty_us": round(graph_us(torch, empty), 3), "load_store_us": round(graph_us(torch, load_store, reps=64), 3)}
+    del src
+    return out
 
 
 def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3) -> None:
@@ -695,6 +791,7 @@ def main() -> int:
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the graph-replay per-op timing")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a 1 GiB device copy (counter runs)")
     ap.add_argument("--no-hbm-ceiling", action="store_true", help="skip the streaming-bandwidth probe")
+    ap.add_argument("--no-launch-floor", action="store_true", help="skip the shortest-launch timing")
     ap.add_argument("--no-low-latency", action="store_true", help="skip the per-expert path on decode")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward ops on the main workload")
     ap.add_argument("--no-router", action="store_true", help="skip the fused router + layout timing")
@@ -788,6 +885,10 @@ def main() -> int:
 
     log("timing a 512 MB device copy (achievable-bandwidth reference)")
     copy_ref = copy_reference(torch)
+    floor = None
+    if not args.no_launch_floor:
+        log("timing the shortest launches (launch floor)")
+        floor = launch_floor(torch)
     ceiling = None
     if not args.no_hbm_ceiling:
         log("measuring streaming bandwidth per read/write mix")
@@ -806,7 +907,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        cpu = cpu_baseline(cfg, W)
+        cpu = cpu_baseline(cfg, W, sec["cfg"] if sec is not None else None)
 
     value = main_res["step_bytes"] / (main_res["ms_per_step"] * 1e-3) / 1e9
     line = {
@@ -835,6 +936,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "copy_reference": copy_ref,
         "hbm_ceiling": ceiling,
+        "launch_floor": floor,
     }
     if sec is not None:
         c2 = sec["cfg"]

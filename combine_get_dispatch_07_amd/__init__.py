@@ -16,7 +16,8 @@ import torch
 from ._lib import (LIB_PATH, MoeError, MoeShape, ll_workspace_bytes, max_recv_rows, moe_combine,  # noqa: F401
                    moe_combine_backward, moe_combine_ll, moe_dispatch, moe_dispatch_backward, moe_dispatch_ll,
                    moe_encode_e4m3, moe_layout_dispatch, moe_layout_dispatch_noalloc, Prepared,
-                   moe_get_dispatch_layout, moe_route_layout, status_string, stream_create_cu_range, stream_destroy,
+                   moe_get_dispatch_layout, moe_route_dispatch, moe_route_layout, status_string, stream_create_cu_range,
+                   stream_destroy,
                    workspace_bytes)
 
 
@@ -83,6 +84,17 @@ def run_layout_dispatch(shape: MoeShape, dtype: str, x: torch.Tensor, topk_idx: 
                         lay["is_token_in_rank"], lay["workspace"], d["recv_x"], d["recv_scales"], d["recv_src_idx"],
                         d["recv_topk_idx"], d["recv_topk_w"], d["rank_offsets"], d["send_row"], d["num_recv"],
                         stream)
+
+
+def run_route_dispatch(shape: MoeShape, dtype: str, logits: torch.Tensor, x: torch.Tensor,
+                       lay: Dict[str, torch.Tensor], d: Dict[str, torch.Tensor], gate: str = "softmax",
+                       num_groups: int = 1, topk_groups: int = 1, stream=None, prepare: bool = False):
+    """run_route then run_dispatch as one call (one kernel up to 1024 tokens); `lay` from alloc_route."""
+    return moe_route_dispatch(shape, dtype, logits, x, lay["topk_idx"], lay["topk_w"], lay["tokens_per_rank"],
+                              lay["tokens_per_expert"], lay["is_token_in_rank"], lay["workspace"], d["recv_x"],
+                              d["recv_scales"], d["recv_src_idx"], d["recv_topk_idx"], d["recv_topk_w"],
+                              d["rank_offsets"], d["send_row"], d["num_recv"], gate, num_groups, topk_groups, stream,
+                              prepare)
 
 
 def prepare_layout(shape: MoeShape, topk_idx: torch.Tensor, lay: Dict[str, torch.Tensor]) -> Prepared:

@@ -76,6 +76,9 @@ def _load() -> ctypes.CDLL:
     lib.moe_get_dispatch_layout.restype = ctypes.c_int
     lib.moe_route_layout.argtypes = [SH, ctypes.POINTER(MoeRouterC), P, P, P, P, P, P, P, SZ, P]
     lib.moe_route_layout.restype = ctypes.c_int
+    lib.moe_route_dispatch.argtypes = [SH, ctypes.POINTER(MoeRouterC), ctypes.c_int, P, P, P, P, P, P, P, P, SZ, I32,
+                                       P, P, P, P, P, P, P, P, P]
+    lib.moe_route_dispatch.restype = ctypes.c_int
     lib.moe_dispatch.argtypes = [SH, ctypes.c_int, P, P, P, P, SZ, I32, P, P, P, P, P, P, P, P, P]
     lib.moe_dispatch.restype = ctypes.c_int
     lib.moe_combine.argtypes = [SH, P, I32, P, P, P, P, P]
@@ -201,6 +204,31 @@ def moe_route_layout(shape: MoeShape, logits, topk_idx, topk_w, tokens_per_rank,
         _ptr(tokens_per_expert, "tokens_per_expert", torch.int32, E),
         _ptr(is_token_in_rank, "is_token_in_rank", torch.uint8, T * R),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel()), stream, prepare, locals())
+
+
+def moe_route_dispatch(shape: MoeShape, dtype: str, logits, x, topk_idx, topk_w, tokens_per_rank, tokens_per_expert,
+                       is_token_in_rank, workspace, recv_x, recv_scales, recv_src_idx, recv_topk_idx, recv_topk_w,
+                       rank_offsets, send_row, num_recv, gate: str = "softmax", num_groups: int = 1,
+                       topk_groups: int = 1, stream=None, prepare: bool = False):
+    T, H, k, E, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts, shape.num_ranks
+    fp8 = DTYPES[dtype] == MOE_FP8_E4M3
+    cap = recv_src_idx.numel()
+    router = MoeRouterC(GATES[gate], int(num_groups), int(topk_groups))
+    return _launch("moe_route_dispatch", (
+        ctypes.byref(shape.c()), ctypes.byref(router), DTYPES[dtype], _ptr(logits, "logits", torch.float32, T * E),
+        _ptr(x, "x", torch.bfloat16, T * H),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
+        _ptr(tokens_per_rank, "tokens_per_rank", torch.int32, R),
+        _ptr(tokens_per_expert, "tokens_per_expert", torch.int32, E),
+        _ptr(is_token_in_rank, "is_token_in_rank", torch.uint8, T * R),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), cap,
+        _ptr(recv_x, "recv_x", torch.uint8 if fp8 else torch.bfloat16, cap * H),
+        _ptr(recv_scales, "recv_scales", torch.float32, cap * (H // 128)) if fp8 else None,
+        _ptr(recv_src_idx, "recv_src_idx", torch.int32, cap),
+        _ptr(recv_topk_idx, "recv_topk_idx", torch.int32, cap * k),
+        _ptr(recv_topk_w, "recv_topk_w", torch.float32, cap * k),
+        _ptr(rank_offsets, "rank_offsets", torch.int32, R + 1),
+        _ptr(send_row, "send_row", torch.int32, T * R), _ptr(num_recv, "num_recv", torch.int32, 1)), stream, prepare, locals())
 
 
 def moe_dispatch(shape: MoeShape, dtype: str, x, topk_idx, topk_w, workspace, recv_x, recv_scales, recv_src_idx,

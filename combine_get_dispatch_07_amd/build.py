@@ -85,16 +85,15 @@ def build_c_client(out: Optional[str] = None) -> str:
     return out
 
 
-HBM_CEILING_SRC = os.path.join(PKG_DIR, "csrc", "hbm_ceiling.hip")
-HBM_CEILING = os.path.join(PKG_DIR, "hbm_ceiling")
+HBM_CEILING_SRC = os.path.join(ROOT, "hbm_ceiling.hip")
+HBM_CEILING = os.path.join(ROOT, "hbm_ceiling")
+LAUNCH_FLOOR_SRC = os.path.join(ROOT, "launch_floor.hip")
+LAUNCH_FLOOR = os.path.join(ROOT, "liblaunch_floor.so")
 
 
-def build_hbm_ceiling(out: Optional[str] = None) -> str:
-    """Compile csrc/hbm_ceiling.hip, the streaming-bandwidth probe bench.py reports beside the
-    kernels' fraction of peak (a standalone HIP program, not part of the library)."""
-    out = out or HBM_CEILING
+def _probe(src: str, out: str, extra) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Wall",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", HBM_CEILING_SRC, "-o", out + ".tmp"]
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *extra, src, "-o", out + ".tmp"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
@@ -102,7 +101,20 @@ def build_hbm_ceiling(out: Optional[str] = None) -> str:
     return out
 
 
+def build_hbm_ceiling(out: Optional[str] = None) -> str:
+    """Compile hbm_ceiling.hip (beside bench.py), the streaming-bandwidth probe bench.py reports
+    beside the kernels' fraction of peak (a standalone HIP program, not part of the library)."""
+    return _probe(HBM_CEILING_SRC, out or HBM_CEILING, [])
+
+
+def build_launch_floor(out: Optional[str] = None) -> str:
+    """Compile launch_floor.hip (beside bench.py): the shortest one-wave launches, which bench.py
+    times next to the decode launches (a measurement aid, not part of the library)."""
+    return _probe(LAUNCH_FLOOR_SRC, out or LAUNCH_FLOOR, ["-shared", "-fPIC"])
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_c_client())
     print(build_hbm_ceiling())
+    print(build_launch_floor())

@@ -142,45 +142,34 @@ __device__ __forceinline__ void store_slice(void* recv_x, float* recv_scales, si
   }
 }
 
-// No load sits under a lane-dependent branch: each is issued from a clamped,
-// always valid address and masked afterwards.  A load under such a branch makes
-// the compiler wait for it before the branch joins, which would serialise the
-// loads (one memory round trip each) in this latency-bound kernel.
+// This lane's U 16-byte pieces of the x slice of `item` (clamped addresses).
 template <int U, bool kFp8>
-__device__ __forceinline__ void dispatch_item(const DispatchArgs& a, int item, int lane) {
-#pragma clang fp contract(off)
+__device__ __forceinline__ void load_item_slice(const DispatchArgs& a, int item, int lane, u32x4 (&v)[U]) {
   const int t = item / a.slices;
-  const int s = item - t * a.slices;
-  const int chunk = t >> 6;
-  const int tt = (chunk << 6) + lane;
-  const int rl = min(lane, a.R - 1);
-  const int c0 = s * (U * kWave) + lane;
+  const int c0 = (item - t * a.slices) * (U * kWave) + lane;
   const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H);
-  const int jl = min(lane, a.k - 1);
-
-  // All loads first: the chunk's rank bitmasks (one per lane), the row of the
-  // chunk's first token on rank lane, the x slice, and the slot metadata (lane
-  // j = slot j).
-  const uint64_t lm_raw = a.token_ranks[min(tt, a.T - 1)];
-  const int cb = a.chunk_base[rl * a.NC + chunk];
-  u32x4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) v[u] = load_source<kFp8>(xrow + min(c0 + u * kWave, a.H8 - 1));
-  // Only the first slice's wave writes the slot metadata.  bf16 rows are split into many slices,
-  // and loading the slots in that wave alone took 0.4-1 us off the prefill copy; for FP8 every
-  // wave loading them measured faster.  The branch is wave-uniform, so no lane waits at its join.
-  int ej_raw = -1;
-  float wj_raw = 0.0f;
-  if (kFp8 || s == 0) {
-    ej_raw = a.topk_idx[(size_t)t * a.k + jl];
-    wj_raw = a.topk_w[(size_t)t * a.k + jl];
-  }
+}
 
-  const uint64_t lm = tt < a.T ? lm_raw : 0ull;
+// Packs item (token t, slice s) once everything it needs is in registers:
+//   v        this lane's pieces of the x slice;
+//   lm       lane l: rank bitmask of token 64 (t / 64) + l of t's chunk (0 past T);
+//   chunk_row lane r < R: receive row of the chunk's first token going to rank r;
+//   ej_raw, wj_raw lane j < k: expert id and weight of slot j (read only when s == 0
+//            for bf16; every wave for FP8).
+// For each destination rank the row is chunk_row + the chunk's tokens before t
+// going to that rank (a ballot); the slice is quantised once if FP8 and stored
+// to every destination; the first slice's wave writes the row metadata and
+// send_row.
+template <int U, bool kFp8>
+__device__ __forceinline__ void pack_item(const DispatchArgs& a, int t, int s, int lane, u32x4 (&v)[U], uint64_t lm,
+                                          int chunk_row, int ej_raw, float wj_raw) {
+#pragma clang fp contract(off)
+  const int c0 = s * (U * kWave) + lane;
   const uint64_t mine = readlane64(lm, t & (kWave - 1)) & a.rank_bits;
   const int tl = t & (kWave - 1);
   const uint64_t lanes_below = tl == 0 ? 0ull : (~0ull >> (kWave - tl));
-  const int chunk_row = lane < a.R ? cb : 0;  // lane r < R: first receive row of this chunk on rank r
 #pragma unroll
   for (int u = 0; u < U; ++u)
     if (c0 + u * kWave >= a.H8) v[u] = u32x4{0u, 0u, 0u, 0u};
@@ -217,6 +206,38 @@ __device__ __forceinline__ void dispatch_item(const DispatchArgs& a, int item, i
     }
   }
   if (meta && lane < a.R) a.send_row[(size_t)t * a.R + lane] = my_row;
+}
+
+// No load sits under a lane-dependent branch: each is issued from a clamped,
+// always valid address and masked afterwards.  A load under such a branch makes
+// the compiler wait for it before the branch joins, which would serialise the
+// loads (one memory round trip each) in this latency-bound kernel.
+template <int U, bool kFp8>
+__device__ __forceinline__ void dispatch_item(const DispatchArgs& a, int item, int lane) {
+  const int t = item / a.slices;
+  const int s = item - t * a.slices;
+  const int chunk = t >> 6;
+  const int tt = (chunk << 6) + lane;
+  const int rl = min(lane, a.R - 1);
+  const int jl = min(lane, a.k - 1);
+
+  // All loads first: the chunk's rank bitmasks (one per lane), the row of the
+  // chunk's first token on rank lane, the x slice, and the slot metadata (lane
+  // j = slot j).
+  const uint64_t lm_raw = a.token_ranks[min(tt, a.T - 1)];
+  const int cb = a.chunk_base[rl * a.NC + chunk];
+  u32x4 v[U];
+  load_item_slice<U, kFp8>(a, item, lane, v);
+  // Only the first slice's wave writes the slot metadata.  bf16 rows are split into many slices,
+  // and loading the slots in that wave alone took 0.4-1 us off the prefill copy; for FP8 every
+  // wave loading them measured faster.  The branch is wave-uniform, so no lane waits at its join.
+  int ej_raw = -1;
+  float wj_raw = 0.0f;
+  if (kFp8 || s == 0) {
+    ej_raw = a.topk_idx[(size_t)t * a.k + jl];
+    wj_raw = a.topk_w[(size_t)t * a.k + jl];
+  }
+  pack_item<U, kFp8>(a, t, s, lane, v, tt < a.T ? lm_raw : 0ull, lane < a.R ? cb : 0, ej_raw, wj_raw);
 }
 
 template <int U, bool kFp8>

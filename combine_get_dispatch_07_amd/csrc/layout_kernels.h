@@ -31,14 +31,21 @@ constexpr int kCountTile = 4096;  // chunk counts staged in LDS per pass of the 
 
 // Words at the start of the workspace that coordinate the blocks of one launch.
 // They are zero between calls: the caller zero-fills a new workspace once, and
-// every launch that uses them leaves them zero again.
+// every launch that uses them leaves them zero again.  Each word has a 4 KiB
+// line of its own: many blocks hit them at once (role and exit tickets, polls
+// of the ready flag), and one shared line would serialise all of them.
+constexpr int kSyncStride = 4096 / sizeof(uint32_t);
 struct SyncWords {
-  uint32_t ticket;  // count blocks finished (last-block-done)
-  uint32_t role;    // role tickets taken (producers + dispatch in one launch)
-  uint32_t ready;   // 1 once the plan of the launch is complete
-  uint32_t exits;   // blocks of the launch that have finished with the sync words
+  uint32_t ticket;  // count (or routing) blocks finished: last-block-done
+  uint32_t pad0[kSyncStride - 1];
+  uint32_t role;    // role tickets taken (routing and dispatch in one launch)
+  uint32_t pad1[kSyncStride - 1];
+  uint32_t exits;   // blocks of that launch that are done with the sync words
+  uint32_t pad2[kSyncStride - 1];
+  uint32_t ready;   // 1 once every routing block of that launch has handed over its tokens
+  uint32_t pad3[kSyncStride - 1];
 };
-constexpr int kSyncBytes = 256;
+constexpr int kSyncBytes = sizeof(SyncWords);
 
 struct LayoutArgs {
   SyncWords* sync;
@@ -52,6 +59,8 @@ struct LayoutArgs {
   int32_t* chunk_base;      // plan: [R, NC] receive row of the chunk's first token on rank r
                             // (per-chunk counts while the count blocks run)
   int32_t* ws_rank_offsets; // plan: [R + 1]
+  int32_t* out_rank_offsets;// [R + 1] and [1]: the dispatch's rank_offsets and num_recv, when the
+  int32_t* out_num_recv;    // layout runs in the same launch as the dispatch (else null)
   uint64_t rank_magic;
   int T, k, E, R, NC, NB;
   int mask_words;           // 1: mask rows written as 32-bit words (R % 4 == 0, aligned)
@@ -137,6 +146,13 @@ __device__ __forceinline__ int publish_rank_offsets(const LayoutArgs& a, int v, 
     a.ws_rank_offsets[lane] = incl - v;
   }
   if (lane == a.R - 1) a.ws_rank_offsets[a.R] = incl;
+  if (a.out_rank_offsets != nullptr) {
+    if (lane < a.R) a.out_rank_offsets[lane] = incl - v;
+    if (lane == a.R - 1) {
+      a.out_rank_offsets[a.R] = incl;
+      *a.out_num_recv = incl;
+    }
+  }
   return incl - v;
 }
 
@@ -282,29 +298,28 @@ __device__ __forceinline__ void finalize_chunk_rows(const LayoutArgs& a, int* ti
   }
 }
 
-// Multi-block path (T > kFusedMaxTokens), one launch: block b counts tokens
-// [256 b, 256 b + 256) -- mask rows, token bitmasks, the counts of its four
-// chunks, rank and expert totals added to the accumulators -- and the block that
-// finishes last turns the counts into receive rows.  Dynamic LDS: hist[E].
+// Multi-block path (T > kFusedMaxTokens): count block b of nblocks counts
+// tokens [256 b, 256 b + 256) -- mask rows, token bitmasks, the counts of its
+// four chunks, rank and expert totals added to the accumulators -- and the
+// block that finishes last turns the counts into receive rows and returns true.
+// Every thread of the block must call it.  hist: E ints of LDS; tile:
+// kCountTile ints; offs: 64 ints.
 template <int KI>
-__global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a) {
+__device__ __forceinline__ bool layout_count_produce(const LayoutArgs& a, int b, int nblocks, int* hist,
+                                                     int (*wave_cnt)[kWave], int* tile, int* offs) {
   constexpr int kChunks = kLayoutBlock / kWave;
-  extern __shared__ int hist[];  // [E]
-  __shared__ int wave_cnt[kChunks][kWave];
-  __shared__ int tile[kCountTile];
-  __shared__ int offs[kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   for (int e = tid; e < a.E; e += kLayoutBlock) hist[e] = 0;
   __syncthreads();
 
-  const int t = blockIdx.x * kLayoutBlock + tid;
+  const int t = b * kLayoutBlock + tid;
   const uint64_t m = token_rank_mask<KI>(a, t, hist);
   if (t < a.T) {
     a.token_ranks[t] = m;
     write_mask_row(a, t, m);
   }
   const int cnt = wave_rank_counts(m, a.R, lane, wave_cnt[wave]);
-  const int chunk = blockIdx.x * kChunks + wave;
+  const int chunk = b * kChunks + wave;
   if (chunk < a.NC && lane < a.R) {
     put_coherent(&a.chunk_base[lane * a.NC + chunk], cnt);
     if (cnt) atomicAdd(&a.rank_acc[lane], cnt);
@@ -313,9 +328,20 @@ __global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a
   for (int e = tid; e < a.E; e += kLayoutBlock)
     if (hist[e]) atomicAdd(&a.expert_acc[e], hist[e]);
 
-  if (!last_block_done(&a.sync->ticket, gridDim.x)) return;
+  if (!last_block_done(&a.sync->ticket, nblocks)) return false;
   finalize_chunk_rows(a, tile, offs);
   if (tid == 0) clear_word(&a.sync->ticket);
+  return true;
+}
+
+// One launch of the multi-block layout.  Dynamic LDS: hist[E].
+template <int KI>
+__global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a) {
+  extern __shared__ int hist[];  // [E]
+  __shared__ int wave_cnt[kLayoutBlock / kWave][kWave];
+  __shared__ int tile[kCountTile];
+  __shared__ int offs[kWave];
+  layout_count_produce<KI>(a, blockIdx.x, gridDim.x, hist, wave_cnt, tile, offs);
 }
 
 }  // namespace moe

@@ -21,6 +21,7 @@
 #include "ll_kernels.h"
 #include "router_kernels.h"
 #include "send_small_kernels.h"
+#include "fused_send_kernels.h"
 
 namespace {
 
@@ -449,6 +450,110 @@ bool launch_send_small(const moe::LayoutArgs& lay, const moe::DispatchArgs& d, b
   return true;
 }
 
+// Router arguments after every check moe_route_layout makes (shape already checked).
+moe_status route_args(const moe_shape& s, const moe_router* router, const float* logits, int32_t* topk_idx,
+                      float* topk_w, int32_t* tokens_per_rank, int32_t* tokens_per_expert, uint8_t* is_token_in_rank,
+                      void* workspace, size_t workspace_bytes, moe::RouterArgs& a) {
+  if (router == nullptr) return MOE_ERR_INVALID_ARG;
+  const int64_t T = s.num_tokens;
+  const int E = s.num_experts, k = s.num_topk, G = router->num_groups, KG = router->topk_groups;
+  if (router->gate != MOE_GATE_SOFTMAX && router->gate != MOE_GATE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (G < 1 || KG < 1 || KG > G) return MOE_ERR_INVALID_ARG;
+  if (E % 8 != 0 || k > moe::kRouterMaxK) return MOE_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return MOE_ERR_UNSUPPORTED;
+  if (E % G != 0 || k > KG * (E / G)) return MOE_ERR_INVALID_ARG;
+  if (!present(logits, T) || !present(topk_idx, T) || !present(topk_w, T) || !present(is_token_in_rank, T) ||
+      !tokens_per_rank || !tokens_per_expert || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(tokens_per_rank, 4) ||
+      !aligned(tokens_per_expert, 4) || !aligned(workspace, kPlanAlign))
+    return MOE_ERR_INVALID_ARG;
+  const PlanLayout p = plan_layout(s);
+  if (workspace_bytes < p.total) return MOE_ERR_INVALID_ARG;
+
+  char* ws = static_cast<char*>(workspace);
+  a = moe::RouterArgs{};
+  a.lay.sync = reinterpret_cast<moe::SyncWords*>(ws + p.sync);
+  a.lay.expert_acc = reinterpret_cast<int32_t*>(ws + p.expert_acc);
+  a.lay.rank_acc = reinterpret_cast<int32_t*>(ws + p.rank_acc);
+  a.logits = logits;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.lay.topk_idx = topk_idx;
+  a.lay.tokens_per_rank = tokens_per_rank;
+  a.lay.tokens_per_expert = tokens_per_expert;
+  a.lay.mask = is_token_in_rank;
+  a.lay.token_ranks = reinterpret_cast<uint64_t*>(ws + p.token_ranks);
+  a.lay.chunk_base = reinterpret_cast<int32_t*>(ws + p.chunk_base);
+  a.lay.ws_rank_offsets = reinterpret_cast<int32_t*>(ws + p.rank_offsets);
+  a.lay.rank_magic = rank_magic(s);
+  a.lay.T = s.num_tokens;
+  a.lay.k = k;
+  a.lay.E = E;
+  a.lay.R = s.num_ranks;
+  a.lay.NC = p.NC;
+  a.lay.NB = p.NC;  // one routing block per 64-token chunk
+  a.lay.mask_words = (s.num_ranks % 4 == 0 && aligned(is_token_in_rank, 4)) ? 1 : 0;
+  a.lay.ids_vec4 = (k % 4 == 0 && aligned(topk_idx, 16)) ? 1 : 0;  // the layout kernel's reads of the ids
+  a.V = E % 16 == 0 ? E / 16 : E / 8;  // experts per lane: 16 or 8 lanes per token
+  a.G = G;
+  a.KG = KG;
+  a.sigmoid = router->gate == MOE_GATE_SIGMOID ? 1 : 0;
+  a.vec4 = (a.V % 4 == 0 && aligned(logits, 16)) ? 1 : 0;
+  return MOE_OK;
+}
+
+void launch_router_any(const moe::RouterArgs& a, hipStream_t stream) {
+  const size_t lds = (size_t)a.lay.E * sizeof(int);
+  if (a.lay.E % 16 == 0)  // 16 lanes per token, one slot per lane
+    launch_router<16, 1>(a.lay.T, lds, stream, a);
+  else if (a.lay.k <= 8)
+    launch_router<8, 1>(a.lay.T, lds, stream, a);
+  else
+    launch_router<8, 2>(a.lay.T, lds, stream, a);
+}
+
+// Routing, layout and dispatch in one launch (route_dispatch_kernel).
+#ifndef MOE_FUSED_ROUTE
+#define MOE_FUSED_ROUTE 1
+#endif
+
+template <int P, int KS, bool kFp8>
+void launch_route_dispatch_t(int U, dim3 grid, hipStream_t stream, const moe::FusedSendArgs& f) {
+  const dim3 block(moe::kFusedWaves * moe::kWave);
+  if (U == 2)
+    hipLaunchKernelGGL((moe::route_dispatch_kernel<P, KS, 2, kFp8>), grid, block, 0, stream, f);
+  else
+    hipLaunchKernelGGL((moe::route_dispatch_kernel<P, KS, 1, kFp8>), grid, block, 0, stream, f);
+}
+
+// 1 <= T <= 1024: the routing blocks (16 or 32 tokens each) and the dispatch
+// blocks of one launch; returns false (nothing launched) outside that range.
+// Dispatch slices are one or two 64-lane groups of 16-byte pieces.
+bool launch_route_dispatch(moe::RouterArgs r, moe::DispatchArgs d, bool fp8, hipStream_t stream) {
+  const int T = d.T;
+  if (!MOE_FUSED_ROUTE || T < 1 || T > moe::kFusedMaxTokens) return false;
+  const int P = r.lay.E % 16 == 0 ? 16 : 8;
+  const int KS = (P == 8 && r.lay.k > 8) ? 2 : 1;
+  const int groups = (d.H8 + moe::kWave - 1) / moe::kWave;
+  const int U = (fp8 && groups >= 2 && (long)T * ((groups + 1) / 2) >= kMinFp8Waves) ? 2 : 1;
+  d.slices = (groups + U - 1) / U;
+  d.items = T * d.slices;
+  r.lay.out_rank_offsets = d.rank_offsets;
+  r.lay.out_num_recv = d.num_recv;
+  moe::FusedSendArgs f{r, d, 0};
+  const int tokens_per_producer = moe::kRouterSmallWaves * moe::kWave / P;
+  f.producers = (T + tokens_per_producer - 1) / tokens_per_producer;
+  const dim3 grid(f.producers + (d.items + moe::kFusedWaves - 1) / moe::kFusedWaves);
+  if (P == 16 && fp8) launch_route_dispatch_t<16, 1, true>(U, grid, stream, f);
+  else if (P == 16) launch_route_dispatch_t<16, 1, false>(U, grid, stream, f);
+  else if (KS == 1 && fp8) launch_route_dispatch_t<8, 1, true>(U, grid, stream, f);
+  else if (KS == 1) launch_route_dispatch_t<8, 1, false>(U, grid, stream, f);
+  else if (fp8) launch_route_dispatch_t<8, 2, true>(U, grid, stream, f);
+  else launch_route_dispatch_t<8, 2, false>(U, grid, stream, f);
+  return true;
+}
+
 // Device memory of moe_layout_dispatch_noalloc: the plan (workspace) kept in a
 // file-scope array, for callers that cannot allocate.  Every device the library
 // runs on holds its own copy until the process ends.  Static device memory is
@@ -530,61 +635,36 @@ moe_status moe_route_layout(const moe_shape* shape, const moe_router* router, co
                             size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (router == nullptr) return MOE_ERR_INVALID_ARG;
-  const moe_shape s = *shape;
-  const int64_t T = s.num_tokens;
-  const int E = s.num_experts, k = s.num_topk, G = router->num_groups, KG = router->topk_groups;
-  if (router->gate != MOE_GATE_SOFTMAX && router->gate != MOE_GATE_SIGMOID) return MOE_ERR_INVALID_ARG;
-  if (G < 1 || KG < 1 || KG > G) return MOE_ERR_INVALID_ARG;
-  if (E % 8 != 0 || k > moe::kRouterMaxK) return MOE_ERR_UNSUPPORTED;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return MOE_ERR_UNSUPPORTED;
-  if (E % G != 0 || k > KG * (E / G)) return MOE_ERR_INVALID_ARG;
-  if (!present(logits, T) || !present(topk_idx, T) || !present(topk_w, T) || !present(is_token_in_rank, T) ||
-      !tokens_per_rank || !tokens_per_expert || !workspace)
-    return MOE_ERR_INVALID_ARG;
-  if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(tokens_per_rank, 4) ||
-      !aligned(tokens_per_expert, 4) || !aligned(workspace, kPlanAlign))
-    return MOE_ERR_INVALID_ARG;
-  const PlanLayout p = plan_layout(s);
-  if (workspace_bytes < p.total) return MOE_ERR_INVALID_ARG;
+  moe::RouterArgs a;
+  st = route_args(*shape, router, logits, topk_idx, topk_w, tokens_per_rank, tokens_per_expert, is_token_in_rank,
+                  workspace, workspace_bytes, a);
+  if (st != MOE_OK) return st;
+  launch_router_any(a, stream);
+  return last_launch_status();
+}
 
-  char* ws = static_cast<char*>(workspace);
-  moe::RouterArgs a{};
-  a.lay.sync = reinterpret_cast<moe::SyncWords*>(ws + p.sync);
-  a.lay.expert_acc = reinterpret_cast<int32_t*>(ws + p.expert_acc);
-  a.lay.rank_acc = reinterpret_cast<int32_t*>(ws + p.rank_acc);
-  a.logits = logits;
-  a.topk_idx = topk_idx;
-  a.topk_w = topk_w;
-  a.lay.topk_idx = topk_idx;
-  a.lay.tokens_per_rank = tokens_per_rank;
-  a.lay.tokens_per_expert = tokens_per_expert;
-  a.lay.mask = is_token_in_rank;
-  a.lay.token_ranks = reinterpret_cast<uint64_t*>(ws + p.token_ranks);
-  a.lay.chunk_base = reinterpret_cast<int32_t*>(ws + p.chunk_base);
-  a.lay.ws_rank_offsets = reinterpret_cast<int32_t*>(ws + p.rank_offsets);
-  a.lay.rank_magic = rank_magic(s);
-  a.lay.T = s.num_tokens;
-  a.lay.k = k;
-  a.lay.E = E;
-  a.lay.R = s.num_ranks;
-  a.lay.NC = p.NC;
-  a.lay.NB = p.NC;  // one routing block per 64-token chunk
-  a.lay.mask_words = (s.num_ranks % 4 == 0 && aligned(is_token_in_rank, 4)) ? 1 : 0;
-  a.lay.ids_vec4 = (k % 4 == 0 && aligned(topk_idx, 16)) ? 1 : 0;  // the layout kernel's reads of the ids
-  a.V = E % 16 == 0 ? E / 16 : E / 8;  // experts per lane: 16 or 8 lanes per token
-  a.G = G;
-  a.KG = KG;
-  a.sigmoid = router->gate == MOE_GATE_SIGMOID ? 1 : 0;
-  a.vec4 = (a.V % 4 == 0 && aligned(logits, 16)) ? 1 : 0;
-
-  const size_t lds = (size_t)E * sizeof(int);
-  if (E % 16 == 0)  // 16 lanes per token, one slot per lane
-    launch_router<16, 1>((int)T, lds, stream, a);
-  else if (k <= 8)
-    launch_router<8, 1>((int)T, lds, stream, a);
-  else
-    launch_router<8, 2>((int)T, lds, stream, a);
+moe_status moe_route_dispatch(const moe_shape* shape, const moe_router* router, moe_dtype dtype, const float* logits,
+                              const void* x, int32_t* topk_idx, float* topk_w, int32_t* tokens_per_rank,
+                              int32_t* tokens_per_expert, uint8_t* is_token_in_rank, void* workspace,
+                              size_t workspace_bytes, int32_t recv_capacity, void* recv_x, float* recv_scales,
+                              int32_t* recv_src_idx, int32_t* recv_topk_idx, float* recv_topk_w,
+                              int32_t* rank_offsets, int32_t* send_row, int32_t* num_recv, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  moe::RouterArgs r;
+  st = route_args(*shape, router, logits, topk_idx, topk_w, tokens_per_rank, tokens_per_expert, is_token_in_rank,
+                  workspace, workspace_bytes, r);
+  if (st != MOE_OK) return st;
+  moe::DispatchArgs d;
+  int U = 1;
+  st = dispatch_args(*shape, dtype, x, topk_idx, topk_w, workspace, workspace_bytes, recv_capacity, recv_x,
+                     recv_scales, recv_src_idx, recv_topk_idx, recv_topk_w, rank_offsets, send_row, num_recv, d, U);
+  if (st != MOE_OK) return st;
+  const bool fp8 = dtype == MOE_FP8_E4M3;
+  if (!launch_route_dispatch(r, d, fp8, stream)) {
+    launch_router_any(r, stream);
+    launch_dispatch_args(d, U, fp8, stream);
+  }
   return last_launch_status();
 }
 

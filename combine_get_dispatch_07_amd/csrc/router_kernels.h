@@ -251,13 +251,13 @@ __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int 
   sum = lanes_sum<P>(sum);
   const uint64_t ranks = ((uint64_t)lanes_or<P>(rhi) << 32) | lanes_or<P>(rlo);
 
-  if (live) {
+  if (live) {  // through the L2: a dispatch in the same launch may read them
 #pragma unroll
     for (int q = 0; q < KS; ++q) {
       const int j = q * P + p;
       if (j < L.k) {
-        a.topk_idx[(size_t)t * L.k + j] = sel[q];
-        a.topk_w[(size_t)t * L.k + j] = ev[q] / sum;
+        put_coherent(&a.topk_idx[(size_t)t * L.k + j], sel[q]);
+        put_coherent(&a.topk_w[(size_t)t * L.k + j], ev[q] / sum);
       }
     }
   } else {
@@ -355,30 +355,47 @@ __device__ __forceinline__ void finalize_small_plan(const LayoutArgs& a, int (*c
   small_chunk_rows(a, cnt, offs);
 }
 
-// 1 <= T <= kFusedMaxTokens: blocks of kRouterSmallWaves waves route
-// kRouterSmallWaves * 64 / P tokens each, write ids, weights, bitmasks (handed
-// to the last block) and mask rows, and add their expert counts to the
-// workspace accumulator; the block that finishes last computes the rest of the
-// plan.
+// 1 <= T <= kFusedMaxTokens: block b of nblocks (kRouterSmallWaves waves)
+// routes tokens [b * TPB, b * TPB + TPB), TPB = kRouterSmallWaves * 64 / P,
+// writes ids, weights, bitmasks (handed to the last block) and mask rows, and
+// adds its expert counts to the workspace accumulator; the block that finishes
+// last computes the rest of the plan and returns true.  Every thread of the
+// block must call it.  offs: 65 ints of LDS (offs[r] = segment offset of rank
+// r, offs[64] = receive rows, valid in the block that returns true).  With
+// kSignal, the last block raises the ready flag as soon as it has drawn its
+// ticket (every routing block's hand-off has completed then), before computing
+// the plan, for others in the same launch; the ticket and the flag are then left
+// for whoever resets the sync words.
+template <int P, int KS, bool kSignal = false>
+__device__ __forceinline__ bool router_small_produce(const RouterArgs& a, int b, int nblocks,
+                                                     int (*cnt)[kWave], int* offs) {
+  constexpr int kThreads = kRouterSmallWaves * kWave;  // routing threads; further waves only join in
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const LayoutArgs& L = a.lay;
+  if (tid < kThreads) {  // whole waves: the others skip the routing instead of running it on no token
+    const int t = b * (kThreads / P) + tid / P;
+    const int p = lane & (P - 1);
+    int sel[KS];
+    const uint64_t m = route_token<P, KS>(a, t, lane, sel);
+#pragma unroll
+    for (int q = 0; q < KS; ++q)
+      if (sel[q] >= 0) atomicAdd(&L.expert_acc[sel[q]], 1);
+    if (p == 0 && t < L.T) put_coherent(&L.token_ranks[t], m);
+    write_token_layout<P, false>(L, t, p, m);
+  }
+
+  if (!last_block_done(&L.sync->ticket, nblocks)) return false;
+  if (kSignal && tid == 0) put_coherent(&L.sync->ready, 1u);
+  finalize_small_plan(L, cnt, offs);
+  if (!kSignal && tid == 0) clear_word(&L.sync->ticket);
+  return true;
+}
+
 template <int P, int KS>
 __global__ __launch_bounds__(kRouterSmallWaves * kWave) void router_small_kernel(RouterArgs a) {
   __shared__ int cnt[kFusedMaxChunks][kWave];
   __shared__ int offs[kWave + 1];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const LayoutArgs& L = a.lay;
-  const int t = blockIdx.x * (kRouterSmallWaves * kWave / P) + tid / P;
-  const int p = lane & (P - 1);
-  int sel[KS];
-  const uint64_t m = route_token<P, KS>(a, t, lane, sel);
-#pragma unroll
-  for (int q = 0; q < KS; ++q)
-    if (sel[q] >= 0) atomicAdd(&L.expert_acc[sel[q]], 1);
-  if (p == 0 && t < L.T) put_coherent(&L.token_ranks[t], m);
-  write_token_layout<P, false>(L, t, p, m);
-
-  if (!last_block_done(&L.sync->ticket, gridDim.x)) return;
-  finalize_small_plan(L, cnt, offs);
-  if (tid == 0) clear_word(&L.sync->ticket);
+  router_small_produce<P, KS>(a, blockIdx.x, gridDim.x, cnt, offs);
 }
 
 }  // namespace moe

@@ -8,7 +8,7 @@
 // 5 reads : 1 write (the combine's mix at top-8 over 8 ranks, ~5.3 rows per
 // token), 1 read : 5 writes (the dispatch's) and 5 reads : 5 writes (close to
 // the combine backward's: g and the token's rows read, one row per rank written).  A measurement aid, not part
-// of the library: bench.py reports it next to the kernels' fraction of peak.
+// of the library: bench.py (beside it) reports it next to the kernels' fraction of peak.
 //
 //   hipcc --offload-arch=gfx950 -O3 hbm_ceiling.hip -o hbm_ceiling && ./hbm_ceiling
 #include <hip/hip_runtime.h>

@@ -163,6 +163,29 @@ moe_status moe_route_layout(const moe_shape* shape, const moe_router* router, co
                             int32_t* tokens_per_expert, uint8_t* is_token_in_rank, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* Routing, layout and dispatch in one call.  [overlap notes, 节点内通信: DeepEP
+ * runs top-k together with the sparse exchange so that no CPU step separates
+ * them.]
+ *
+ * Writes everything moe_route_layout and then moe_dispatch (on the ids and
+ * weights just computed) write for the same arguments -- topk_idx, topk_w,
+ * tokens_per_rank, tokens_per_expert, is_token_in_rank, the plan in
+ * `workspace`, the receive rows and their metadata, rank_offsets, send_row and
+ * num_recv -- with identical values.  Arguments, limits and errors are the
+ * union of the two calls' (topk_idx and topk_w are outputs here).  For
+ * 1 <= T <= 1024 one kernel does all of it: its first blocks route, the last of
+ * them to finish completes the plan, and the remaining blocks, which load
+ * their rows of x meanwhile, pack the rows once the plan is complete (no
+ * block waits for a block that could be waiting itself); otherwise the two
+ * calls' launches run back to back.
+ */
+moe_status moe_route_dispatch(const moe_shape* shape, const moe_router* router, moe_dtype dtype, const float* logits,
+                              const void* x, int32_t* topk_idx, float* topk_w, int32_t* tokens_per_rank,
+                              int32_t* tokens_per_expert, uint8_t* is_token_in_rank, void* workspace,
+                              size_t workspace_bytes, int32_t recv_capacity, void* recv_x, float* recv_scales,
+                              int32_t* recv_src_idx, int32_t* recv_topk_idx, float* recv_topk_w,
+                              int32_t* rank_offsets, int32_t* send_row, int32_t* num_recv, hipStream_t stream);
+
 /* Dispatch.  [overlap notes, 节点内通信: filtered send, FP8 transport;
  * rocSHMEM notes 3.2: rows packed into a preallocated receive buffer.]
  *

@@ -152,3 +152,33 @@ def dispatch_with_plan(res: PathResult, x: np.ndarray, dtype: str = "bf16") -> P
         out[key] = d[key].cpu().numpy()
     out["recv_x"] = bf16_to_np(d["recv_x"]) if dtype == "bf16" else d["recv_x"].cpu().numpy()
     return out
+
+
+def run_route_dispatch(logits: np.ndarray, x: np.ndarray, k: int, E: int, R: int, dtype: str, gate: str = "softmax",
+                       num_groups: int = 1, topk_groups: int = 1, guard: int = GUARD_ROWS, calls: int = 1,
+                       lay=None) -> PathResult:
+    """moe_route_dispatch (routing, layout and dispatch in one call) on fp32 logits [T, E] and bf16 x;
+    `calls` back-to-back calls on the same buffers (the last one's outputs are returned); `lay` reuses
+    an earlier result's workspace and routing buffers."""
+    T, H = x.shape
+    shape = moe.MoeShape(T, H, k, E, R)
+    ld = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).cuda().view(T, E)
+    xd = to_dev_bf16(x) if T else torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    lay = moe.alloc_route(shape) if lay is None else lay
+    _poison(lay)
+    d = moe.alloc_dispatch(shape, dtype, capacity=moe.max_recv_rows(shape) + guard)
+    _poison(d)
+    for _ in range(calls):
+        moe.run_route_dispatch(shape, dtype, ld, xd, lay, d, gate, num_groups, topk_groups)
+    torch.cuda.synchronize()
+    r = PathResult()
+    r["shape"] = shape
+    for key in ("topk_idx", "topk_w", "tokens_per_rank", "tokens_per_expert", "is_token_in_rank"):
+        r[key] = lay[key].cpu().numpy()
+    for key in ("recv_src_idx", "recv_topk_idx", "recv_topk_w", "rank_offsets", "send_row", "num_recv"):
+        r[key] = d[key].cpu().numpy()
+    r["recv_x"] = bf16_to_np(d["recv_x"]) if dtype == "bf16" else d["recv_x"].cpu().numpy()
+    if dtype == "fp8":
+        r["recv_scales"] = d["recv_scales"].cpu().numpy()
+    r["_dev"] = {"logits": ld, "x": xd, "lay": lay, "d": d}
+    return r

@@ -66,7 +66,7 @@ def test_sizes():
     assert L.max_recv_rows(L.MoeShape(100, 256, 8, 16, 3)) == -1  # E % R != 0
     ws = L.workspace_bytes(L.MoeShape(4096, 7168, 8, 256, 8))
     # sync words + expert and rank accumulators + token bitmasks + chunk rows + offsets, each 256-aligned
-    assert ws >= 256 + 256 * 4 + 8 * 4 + 4096 * 8 + 8 * 64 * 4 + 9 * 4 and ws % 256 == 0
+    assert ws >= 4 * 4096 + 256 * 4 + 8 * 4 + 4096 * 8 + 8 * 64 * 4 + 9 * 4 and ws % 256 == 0
     assert L.workspace_bytes(L.MoeShape(0, 256, 1, 4, 4)) > 0
     assert L.workspace_bytes(L.MoeShape(-1, 256, 1, 4, 4)) == 0
 

@@ -5,7 +5,8 @@ Bar: every output of moe_get_dispatch_layout + moe_dispatch bit-identical (count
 offsets, send_row, num_recv, receive rows, FP8 scales, row metadata), rows at or beyond num_recv
 untouched, and the plan left in the workspace valid: moe_dispatch run again from it reproduces the
 receive buffers.  Cases cover the one-kernel form (both slice widths, 8 and 32 ids per lane, one to
-sixteen 64-token batches) and the fallback to two launches.
+sixteen 64-token batches) and the two launches above 1024 tokens (every FP8 slice width, up to 274
+count blocks, 64 ranks, 32 ids) or above hidden 16384.
 """
 import numpy as np
 import pytest
@@ -94,6 +95,14 @@ def test_decode_workload():
     run_fused_case(d["x"], d["topk_idx"], d["topk_w"], cfg.num_experts, cfg.num_ranks, cfg.dispatch_dtype)
 
 
+@pytest.mark.parametrize("name", ["prefill", "group_limited"])
+def test_large_workloads(name):
+    """Full-size workloads through the two launches (bf16 prefill; FP8 at 64 ranks)."""
+    cfg = W.CONFIG_BY_NAME[name]
+    d = W.make_inputs(cfg)
+    run_fused_case(d["x"], d["topk_idx"], d["topk_w"], cfg.num_experts, cfg.num_ranks, cfg.dispatch_dtype)
+
+
 def test_tiny_workload():
     cfg = W.CONFIG_BY_NAME["tiny"]
     d = W.make_inputs(cfg)
@@ -112,6 +121,12 @@ CASES = [
     ("fallback_wide", 8, 64, 16896, 16, 4, 4, "bf16", 0.1),       # 33 groups: two launches
     ("one_rank", 9, 77, 256, 8, 2, 1, "bf16", 0.0),
     ("R_not_multiple_of_4", 10, 333, 256, 30, 5, 6, "fp8", 0.1),
+    # above 1024 tokens: the one-launch layout, then the dispatch
+    ("two_launch_many_blocks", 11, 70000, 64, 64, 4, 8, "bf16", 0.05),  # 274 count blocks
+    ("two_launch_fp8_width4", 12, 1500, 7168, 256, 8, 8, "fp8", 0.02),
+    ("two_launch_fp8_width7", 13, 3000, 7168, 256, 8, 32, "fp8", 0.02),
+    ("two_launch_R64", 14, 2000, 256, 256, 8, 64, "bf16", 0.0),
+    ("two_launch_k32", 15, 1100, 128, 512, 32, 16, "fp8", 0.1),
 ]
 
 
