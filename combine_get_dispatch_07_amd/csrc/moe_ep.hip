@@ -156,17 +156,56 @@ int device_cu_count() {
   return cus;
 }
 
-// Compute units a launch on `stream` can use: the popcount of the stream's CU
-// mask (all of the device's CUs for an unrestricted stream).
-int stream_cu_count(hipStream_t stream) {
-  uint32_t mask[kMaxCuMaskWords] = {0};
-  if (stream == nullptr || hipExtStreamGetCUMask(stream, kMaxCuMaskWords, mask) != hipSuccess) {
-    (void)hipGetLastError();
-    return device_cu_count();
+// Streams made by moe_stream_create_cu_range and the number of CUs each may
+// use, so that a launch learns its stream's CU budget from a table lookup
+// instead of asking the runtime for the stream's mask on every call.  Slots are
+// claimed and released with compare-and-swap; a lookup scans them only while
+// some stream is registered.
+constexpr int kMaxCuStreams = 64;
+struct CuStream {
+  std::atomic<hipStream_t> stream{nullptr};
+  std::atomic<int> cus{0};
+};
+CuStream g_cu_streams[kMaxCuStreams];
+std::atomic<int> g_cu_stream_count{0};
+
+bool register_cu_stream(hipStream_t stream, int cus) {
+  for (CuStream& slot : g_cu_streams) {
+    hipStream_t empty = nullptr;
+    if (slot.stream.load(std::memory_order_relaxed) == nullptr &&
+        slot.stream.compare_exchange_strong(empty, stream, std::memory_order_acq_rel)) {
+      slot.cus.store(cus, std::memory_order_release);
+      g_cu_stream_count.fetch_add(1, std::memory_order_acq_rel);
+      return true;
+    }
   }
-  int n = 0;
-  for (uint32_t w : mask) n += __builtin_popcount(w);
-  return n > 0 ? std::min(n, device_cu_count()) : device_cu_count();
+  return false;
+}
+
+void unregister_cu_stream(hipStream_t stream) {
+  for (CuStream& slot : g_cu_streams) {
+    hipStream_t s = stream;
+    if (slot.stream.load(std::memory_order_acquire) == stream) {
+      slot.cus.store(0, std::memory_order_relaxed);
+      if (slot.stream.compare_exchange_strong(s, nullptr, std::memory_order_acq_rel))
+        g_cu_stream_count.fetch_sub(1, std::memory_order_acq_rel);
+      return;
+    }
+  }
+}
+
+// Compute units a launch on `stream` can use: the registered budget of a
+// stream made by moe_stream_create_cu_range, else all of the device's CUs.
+int stream_cu_count(hipStream_t stream) {
+  if (stream != nullptr && g_cu_stream_count.load(std::memory_order_acquire) > 0) {
+    for (const CuStream& slot : g_cu_streams) {
+      if (slot.stream.load(std::memory_order_acquire) == stream) {
+        const int cus = slot.cus.load(std::memory_order_acquire);
+        if (cus > 0) return std::min(cus, device_cu_count());
+      }
+    }
+  }
+  return device_cu_count();
 }
 
 int device_xcc_count() {
@@ -1019,11 +1058,17 @@ moe_status moe_stream_create_cu_range(int32_t first_cu, int32_t num_cus, hipStre
     *stream = nullptr;
     return MOE_ERR_HIP;
   }
+  if (!register_cu_stream(*stream, num_cus)) {  // more than kMaxCuStreams alive at once
+    (void)hipStreamDestroy(*stream);
+    *stream = nullptr;
+    return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
 moe_status moe_stream_destroy(hipStream_t stream) {
   if (stream == nullptr) return MOE_ERR_INVALID_ARG;
+  unregister_cu_stream(stream);
   return hipStreamDestroy(stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -385,8 +385,11 @@ moe_status moe_dispatch_backward(const moe_shape* shape, const void* grad_recv_x
  * kernels a fixed share of the SMs (20 of 132) so that expert computation
  * overlaps on the rest; DeepEP overview: Buffer.set_num_sms trades exchange
  * latency against compute.]  The MI355X equivalent is a stream whose kernels
- * may only run on a chosen set of CUs.  Launches of this library on such a
- * stream size their persistent grids to that stream's CUs.
+ * may only run on a chosen set of CUs.  Launches of this library on a stream
+ * made by moe_stream_create_cu_range size their persistent grids to that
+ * stream's CUs (looked up in a table the library keeps, not queried from the
+ * runtime per call); any other stream counts as unrestricted (results are
+ * the same either way; only the grid size differs).
  *
  * CU-mask bit i of a stream belongs to XCD (i mod number of XCDs) on MI355X,
  * and every XCD must keep at least one CU; so the range [first_cu,
@@ -398,7 +401,8 @@ moe_status moe_dispatch_backward(const moe_shape* shape, const void* grad_recv_x
  * [first_cu, first_cu + num_cus) of the current device.  first_cu == 0 with
  * num_cus <= 0 or >= the CU count gives an unrestricted stream.  The caller
  * destroys it with moe_stream_destroy.  MOE_ERR_INVALID_ARG for a range that
- * is not a multiple of the XCD count or exceeds the device. */
+ * is not a multiple of the XCD count or exceeds the device;
+ * MOE_ERR_UNSUPPORTED with 64 restricted streams already alive. */
 moe_status moe_stream_create_cu_range(int32_t first_cu, int32_t num_cus, hipStream_t* stream);
 
 /* Destroys a stream made by moe_stream_create_cu_range. */

@@ -11,12 +11,17 @@
  *   - the dispatch backward of the received rows is x times the number of distinct ranks;
  *   - E4M3 codes of exactly representable values, ties and signed zero are known;
  *   - layout and dispatch as one call (moe_layout_dispatch) give the two calls' rows and handle.
+ * It also times the host side of each entry point: 1000 calls enqueued back to back with no
+ * synchronisation inside the loop, printed as "host_us_per_call <name> <microseconds>" (argument
+ * checks plus kernel enqueue; the GPU work itself is not waited for).
  * Exit status 0 on success; prints what failed otherwise.
  */
+#define _POSIX_C_SOURCE 199309L
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+#include <time.h>
 
 #include "moe_ep.h"
 
@@ -233,6 +238,65 @@ int main(void) {
       ++fails;
     }
   }
+  /* host cost per call: reps enqueues of one entry point, no synchronisation in the loop */
+  {
+    enum { REPS = 1000 };
+    static float logits[T * E];
+    for (int i = 0; i < T * E; ++i) logits[i] = (float)((i * 37) % 101) / 101.0f;
+    float *dlog, *dw2;
+    int32_t *didx2, *dtpr3, *dtpe3;
+    uint8_t* dmask3;
+    void* dws3;
+    CHECK_HIP(hipMalloc((void**)&dlog, sizeof(logits)));
+    CHECK_HIP(hipMalloc((void**)&dw2, sizeof(w)));
+    CHECK_HIP(hipMalloc((void**)&didx2, sizeof(idx)));
+    CHECK_HIP(hipMalloc((void**)&dtpr3, R * sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&dtpe3, E * sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&dmask3, T * R));
+    CHECK_HIP(hipMalloc(&dws3, ws_bytes));
+    CHECK_HIP(hipMemset(dws3, 0, ws_bytes));
+    CHECK_HIP(hipMemcpy(dlog, logits, sizeof(logits), hipMemcpyHostToDevice));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    const moe_router router = {MOE_GATE_SOFTMAX, 1, 1};
+    struct timespec t0, t1;
+#define TIME_CALLS(name, call)                                                                          \
+  do {                                                                                                 \
+    clock_gettime(CLOCK_MONOTONIC, &t0);                                                               \
+    for (int i_ = 0; i_ < REPS; ++i_) CHECK_MOE(call);                                                 \
+    clock_gettime(CLOCK_MONOTONIC, &t1);                                                               \
+    CHECK_HIP(hipStreamSynchronize(stream));                                                           \
+    printf("host_us_per_call %s %.3f\n", name,                                                         \
+           ((double)(t1.tv_sec - t0.tv_sec) * 1e6 + (double)(t1.tv_nsec - t0.tv_nsec) / 1e3) / REPS);   \
+  } while (0)
+    clock_gettime(CLOCK_MONOTONIC, &t0);
+    for (int i = 0; i < REPS; ++i) CHECK_HIP(hipMemsetAsync(dfq, 0, 4, stream));
+    clock_gettime(CLOCK_MONOTONIC, &t1);
+    CHECK_HIP(hipStreamSynchronize(stream));
+    printf("host_us_per_call hipMemsetAsync_4_bytes %.3f\n",
+           ((double)(t1.tv_sec - t0.tv_sec) * 1e6 + (double)(t1.tv_nsec - t0.tv_nsec) / 1e3) / REPS);
+    TIME_CALLS("moe_get_dispatch_layout", moe_get_dispatch_layout(&shape, didx, dtpr, dtpe, dmask, dws, ws_bytes,
+                                                                  stream));
+    TIME_CALLS("moe_dispatch", moe_dispatch(&shape, MOE_BF16, dx, didx, dw, dws, ws_bytes, cap, drecv, NULL, dsrc,
+                                            dridx, drw, doffs, dsend, dn, stream));
+    TIME_CALLS("moe_layout_dispatch", moe_layout_dispatch(&shape, MOE_BF16, dx, didx, dw, dtpr, dtpe, dmask, dws,
+                                                          ws_bytes, cap, drecv, NULL, dsrc, dridx, drw, doffs,
+                                                          dsend, dn, stream));
+    TIME_CALLS("moe_combine", moe_combine(&shape, drecv, n, didx, dw, dsend, dout, stream));
+    TIME_CALLS("moe_dispatch_backward", moe_dispatch_backward(&shape, drecv, n, NULL, didx, dsend, dgx, NULL,
+                                                              stream));
+    TIME_CALLS("moe_dispatch_ll", moe_dispatch_ll(&shape, MOE_BF16, dx, didx, dllws, ll_ws, T, dllx, NULL, dllsrc,
+                                                  dllcnt, dllpos, stream));
+    TIME_CALLS("moe_combine_ll", moe_combine_ll(&shape, dllx, T, didx, dw, dllpos, dllout, stream));
+    TIME_CALLS("moe_encode_e4m3", moe_encode_e4m3(dfv, dfq, 10, stream));
+    TIME_CALLS("moe_route_layout", moe_route_layout(&shape, &router, dlog, didx2, dw2, dtpr3, dtpe3, dmask3, dws3,
+                                                    ws_bytes, stream));
+    TIME_CALLS("moe_route_dispatch", moe_route_dispatch(&shape, &router, MOE_BF16, dlog, dx, didx2, dw2, dtpr3,
+                                                        dtpe3, dmask3, dws3, ws_bytes, cap, drecv, NULL, dsrc,
+                                                        dridx, drw, doffs, dsend, dn, stream));
+#undef TIME_CALLS
+    hipFree(dlog); hipFree(dw2); hipFree(didx2); hipFree(dtpr3); hipFree(dtpe3); hipFree(dmask3); hipFree(dws3);
+  }
+
   hipFree(dgx); hipFree(dllws); hipFree(dllx); hipFree(dllsrc); hipFree(dllcnt); hipFree(dllpos); hipFree(dllout);
   hipFree(dfv); hipFree(dfq);
   hipFree(dx); hipFree(didx); hipFree(dw); hipFree(dtpr); hipFree(dtpe); hipFree(dmask); hipFree(dws);

@@ -20,3 +20,7 @@ def test_c_client_layout_dispatch_combine():
     r = subprocess.run([CLIENT], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "match" in r.stdout
+    # the host cost of each entry point (enqueue only), for the record
+    costs = [line for line in r.stdout.splitlines() if line.startswith("host_us_per_call")]
+    assert len(costs) == 11, r.stdout
+    print("\n".join(costs), flush=True)
