@@ -30,7 +30,10 @@ __device__ __forceinline__ u32x4 load_source(const u32x4* p) {
     return *p;
 }
 
-constexpr int kDispatchBlock = 256;  // 4 waves, 4 work items per block
+#ifndef MOE_DISPATCH_BLOCK
+#define MOE_DISPATCH_BLOCK 256
+#endif
+constexpr int kDispatchBlock = MOE_DISPATCH_BLOCK;  // 4 waves: 4 work items per block
 constexpr int kFp8Block = 128;       // channels per FP8 scale
 constexpr float kAmaxFloor = 1e-4f;
 constexpr float kE4m3Max = 448.0f;

@@ -210,3 +210,72 @@ def test_graph_replays_one_call_send_side():
     outputs = [lay["tokens_per_rank"], lay["tokens_per_expert"], lay["is_token_in_rank"], d["rank_offsets"],
                d["send_row"], d["num_recv"], d["recv_src_idx"][:n], d["recv_x"][:n], d["recv_scales"][:n], out]
     _replay_check(step, outputs, "one-call send side")
+
+
+@pytest.mark.parametrize("name,T", [("decode", 128), ("prefill", 2048)])
+def test_graph_replays_route_dispatch(name, T):
+    """moe_route_dispatch (one kernel at decode size: its sync words must come back to zero after every
+    launch, graph replays included) + moe_combine in a graph; 2048 tokens take the two-launch form."""
+    import combine_get_dispatch_07_amd as moe
+    from tests.gpu_harness import to_dev_bf16
+
+    cfg = W.with_tokens(W.CONFIG_BY_NAME[name], T)
+    print(f"[case] graph route+dispatch {name} T={T}", flush=True)
+    gate = "sigmoid" if cfg.routing == "sigmoid" else "softmax"
+    dtype = cfg.dispatch_dtype
+    shape = moe.MoeShape(cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks)
+    logits = torch.from_numpy(W.config_logits(cfg)).cuda()
+    x = to_dev_bf16(W.make_inputs(cfg)["x"])
+    lay, d, out = _buffers(moe, shape, dtype, True)
+    y = to_dev_bf16(W.draw_expert_outputs(np.random.default_rng(7), shape.num_tokens * min(shape.num_topk,
+                                                                                              shape.num_ranks),
+                                          shape.hidden))
+
+    def step():
+        moe.run_route_dispatch(shape, dtype, logits, x, lay, d, gate)
+        moe.moe_combine(shape, y, lay["topk_idx"], lay["topk_w"], d["send_row"], out)
+
+    step()
+    torch.cuda.synchronize()
+    n = int(d["num_recv"].item())
+    outputs = [lay["topk_idx"], lay["topk_w"], lay["tokens_per_rank"], lay["tokens_per_expert"],
+               lay["is_token_in_rank"], d["rank_offsets"], d["send_row"], d["num_recv"], d["recv_src_idx"][:n],
+               d["recv_topk_idx"][:n], d["recv_topk_w"][:n], d["recv_x"][:n], out]
+    if dtype == "fp8":
+        outputs.append(d["recv_scales"][:n])
+    _replay_check(step, outputs, f"route+dispatch {name}")
+
+
+@pytest.mark.parametrize("name,T", [("decode", 128), ("prefill", 2048)])
+def test_graph_replays_noalloc_send_side(name, T):
+    """moe_layout_dispatch_noalloc -- for callers under graph capture, which cannot allocate -- + moe_combine
+    in a graph, against the same eager calls."""
+    import combine_get_dispatch_07_amd as moe
+    from tests.gpu_harness import to_dev_bf16
+
+    cfg = W.with_tokens(W.CONFIG_BY_NAME[name], T)
+    print(f"[case] graph no-alloc send side {name} T={T}", flush=True)
+    dtype = cfg.dispatch_dtype
+    shape = moe.MoeShape(cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks)
+    inp = W.make_inputs(cfg)
+    x = to_dev_bf16(inp["x"])
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    w = torch.from_numpy(inp["topk_w"]).cuda()
+    lay, d, out = _buffers(moe, shape, dtype, False)
+    y = to_dev_bf16(W.draw_expert_outputs(np.random.default_rng(8), shape.num_tokens * min(shape.num_topk,
+                                                                                              shape.num_ranks),
+                                          shape.hidden))
+
+    def step():
+        moe.moe_layout_dispatch_noalloc(shape, dtype, x, idx, w, lay["tokens_per_rank"], lay["tokens_per_expert"],
+                                        lay["is_token_in_rank"], d["recv_x"], d["recv_scales"], d["recv_src_idx"],
+                                        d["recv_topk_idx"], d["recv_topk_w"], d["rank_offsets"], d["send_row"],
+                                        d["num_recv"])
+        moe.moe_combine(shape, y, idx, w, d["send_row"], out)
+
+    step()
+    torch.cuda.synchronize()
+    n = int(d["num_recv"].item())
+    outputs = [lay["tokens_per_rank"], lay["tokens_per_expert"], lay["is_token_in_rank"], d["rank_offsets"],
+               d["send_row"], d["num_recv"], d["recv_src_idx"][:n], d["recv_x"][:n], out]
+    _replay_check(step, outputs, f"no-alloc send side {name}")
