@@ -119,16 +119,27 @@ __device__ __forceinline__ void write_mask_row(const LayoutArgs& a, int t, uint6
 }
 
 // Adds each lane's rank bits m to the per-rank counters cnt[0..63] (LDS)
-// with one atomic add per set bit: at most min(k, R) adds per lane, where one
-// ballot per rank would take R dependent steps.  Integer adds: the result
+// with one atomic add per set bit: at most min(k, R) adds per lane, fewer
+// steps than one ballot per rank when R is large.  Integer adds: the result
 // does not depend on their order.
 __device__ __forceinline__ void add_rank_bits(uint64_t m, int* cnt) {
   for (uint64_t b = m; b; b &= b - 1) atomicAdd(&cnt[__builtin_ctzll(b)], 1);
 }
 
 // Lane r (< R) returns how many lanes of the wave have bit r set in m; `cnt`
-// is 64 ints of LDS private to the wave.
+// is 64 ints of LDS private to the wave.  Up to kBallotRanks ranks: one ballot
+// per rank (scalar work, no LDS); above, one LDS atomic per set bit, where the
+// set bits of all lanes hit the same few counters far less often.
+constexpr int kBallotRanks = 16;
 __device__ __forceinline__ int wave_rank_counts(uint64_t m, int R, int lane, int* cnt) {
+  if (R <= kBallotRanks) {
+    int mine = 0;
+    for (int r = 0; r < R; ++r) {
+      const int c = __popcll(__ballot((m >> r) & 1ull));
+      mine = lane == r ? c : mine;
+    }
+    return mine;
+  }
   cnt[lane] = 0;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   add_rank_bits(m, cnt);
@@ -240,6 +251,11 @@ __device__ __forceinline__ void clear_word(uint32_t* w) { put_coherent(w, 0u); }
 template <int kBatch>
 __device__ __forceinline__ void load_count_batch(const LayoutArgs& a, int (&v)[kBatch], int i0, int stride, int n,
                                                  int nc, int c0) {
+  if (nc == a.NC) {  // the tile holds every chunk: element i is chunk_base[i] (no division)
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = get_coherent(&a.chunk_base[min(i0 + u * stride, n - 1)]);
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < kBatch; ++u) {
     const int i = min(i0 + u * stride, n - 1);

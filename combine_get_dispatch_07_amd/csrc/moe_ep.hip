@@ -125,13 +125,13 @@ void launch_dispatch(int U, dim3 grid, hipStream_t stream, const moe::DispatchAr
 #endif
 static_assert(MOE_BWD_WAVES >= 1 && MOE_BWD_WAVES <= moe::kBwdMaxWaves, "waves per block");
 
-// Resident combine waves per CU in the persistent launch: one block of 4
-// waves, one per SIMD, each with two items' payload in flight.  Fewer
-// concurrent streams keep the rows being read at any time close together.
 // Small-batch low-latency dispatch in one launch (0: always the two-pass path).
 #ifndef MOE_LL_SMALL
 #define MOE_LL_SMALL 1
 #endif
+// Resident combine waves per CU in the persistent launch: one block of 4
+// waves, one per SIMD, each with two items' payload in flight.  Fewer
+// concurrent streams keep the rows being read at any time close together.
 #ifndef MOE_COMBINE_WAVES_PER_CU
 #define MOE_COMBINE_WAVES_PER_CU 4
 #endif
