@@ -330,10 +330,6 @@ __device__ __forceinline__ bool layout_count_produce(const LayoutArgs& a, int b,
 
   const int t = b * kLayoutBlock + tid;
   const uint64_t m = token_rank_mask<KI>(a, t, hist);
-  if (t < a.T) {
-    a.token_ranks[t] = m;
-    write_mask_row(a, t, m);
-  }
   const int cnt = wave_rank_counts(m, a.R, lane, wave_cnt[wave]);
   const int chunk = b * kChunks + wave;
   if (chunk < a.NC && lane < a.R) {
@@ -343,6 +339,13 @@ __device__ __forceinline__ bool layout_count_produce(const LayoutArgs& a, int b,
   __syncthreads();
   for (int e = tid; e < a.E; e += kLayoutBlock)
     if (hist[e]) atomicAdd(&a.expert_acc[e], hist[e]);
+  // The plain output stores come last: the compiler waits for outstanding
+  // stores before reusing their registers, and here that wait is the one the
+  // ticket needs anyway rather than a round trip of its own mid-block.
+  if (t < a.T) {
+    a.token_ranks[t] = m;
+    write_mask_row(a, t, m);
+  }
 
   if (!last_block_done(&a.sync->ticket, nblocks)) return false;
   finalize_chunk_rows(a, tile, offs);

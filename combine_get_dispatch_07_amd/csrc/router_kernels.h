@@ -145,11 +145,13 @@ __device__ __forceinline__ void list_fill(uint32_t (&lk)[KL], int (&li)[KL], con
   }
 }
 
-// Routes token t with the P lanes of its lane group: writes its ids and
-// weights; returns its rank bitmask (same in the P lanes; 0 for t >= T) and
-// the expert ids of the lane's slots j = q * P + p in `sel` (-1: none).
+// Routes token t with the P lanes of its lane group: returns its rank bitmask
+// (same in the P lanes; 0 for t >= T), the expert ids of the lane's slots
+// j = q * P + p in `sel` (-1: none) and their weights in `wt`; store_route
+// writes the last two.
 template <int P, int KS>
-__device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int lane, int (&sel)[KS]) {
+__device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int lane, int (&sel)[KS],
+                                                float (&wt)[KS]) {
 #pragma clang fp contract(off)
   constexpr int KL = kRouterList;
   const LayoutArgs& L = a.lay;
@@ -251,20 +253,30 @@ __device__ __forceinline__ uint64_t route_token(const RouterArgs& a, int t, int 
   sum = lanes_sum<P>(sum);
   const uint64_t ranks = ((uint64_t)lanes_or<P>(rhi) << 32) | lanes_or<P>(rlo);
 
-  if (live) {  // through the L2: a dispatch in the same launch may read them
 #pragma unroll
-    for (int q = 0; q < KS; ++q) {
-      const int j = q * P + p;
-      if (j < L.k) {
-        put_coherent(&a.topk_idx[(size_t)t * L.k + j], sel[q]);
-        put_coherent(&a.topk_w[(size_t)t * L.k + j], ev[q] / sum);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < KS; ++q) sel[q] = -1;
+  for (int q = 0; q < KS; ++q) {
+    wt[q] = ev[q] / sum;
+    sel[q] = live ? sel[q] : -1;
   }
   return live ? ranks : 0;
+}
+
+// Writes the ids and weights route_token returned for token t (lane p of its
+// P lanes holds slots q * P + p), through the L2: a dispatch in the same launch
+// may read them.
+template <int P, int KS>
+__device__ __forceinline__ void store_route(const RouterArgs& a, int t, int p, const int (&sel)[KS],
+                                            const float (&wt)[KS]) {
+  const LayoutArgs& L = a.lay;
+  if (t >= L.T) return;
+#pragma unroll
+  for (int q = 0; q < KS; ++q) {
+    const int j = q * P + p;
+    if (j < L.k) {
+      put_coherent(&a.topk_idx[(size_t)t * L.k + j], sel[q]);
+      put_coherent(&a.topk_w[(size_t)t * L.k + j], wt[q]);
+    }
+  }
 }
 
 // Writes token t's rank bitmask (lane p == 0 of its P lanes) and its
@@ -306,12 +318,16 @@ __global__ __launch_bounds__(kWave * P) void router_count_kernel(RouterArgs a) {
   const int t = blockIdx.x * kWave + tw;
   const int p = lane & (P - 1);
   int sel[KS];
-  const uint64_t m = route_token<P, KS>(a, t, lane, sel);
+  float wt[KS];
+  const uint64_t m = route_token<P, KS>(a, t, lane, sel, wt);
 #pragma unroll
   for (int q = 0; q < KS; ++q)
     if (sel[q] >= 0) atomicAdd(&hist[sel[q]], 1);
-  write_token_layout<P>(L, t, p, m);
   if (p == 0) add_rank_bits(m, chunk_cnt);
+  // every store after the counting: the compiler waits for outstanding stores
+  // before reusing their registers, which would stall the counting on them
+  write_token_layout<P>(L, t, p, m);
+  store_route<P, KS>(a, t, p, sel, wt);
   __syncthreads();
 
   // what the last block reads: the chunk's counts and the totals
@@ -376,12 +392,16 @@ __device__ __forceinline__ bool router_small_produce(const RouterArgs& a, int b,
     const int t = b * (kThreads / P) + tid / P;
     const int p = lane & (P - 1);
     int sel[KS];
-    const uint64_t m = route_token<P, KS>(a, t, lane, sel);
+    float wt[KS];
+    const uint64_t m = route_token<P, KS>(a, t, lane, sel, wt);
+    // the mask row first: its loop reuses registers, and the compiler waits
+    // for outstanding stores before reusing theirs
+    write_token_layout<P, false>(L, t, p, m);
+    if (p == 0 && t < L.T) put_coherent(&L.token_ranks[t], m);
 #pragma unroll
     for (int q = 0; q < KS; ++q)
       if (sel[q] >= 0) atomicAdd(&L.expert_acc[sel[q]], 1);
-    if (p == 0 && t < L.T) put_coherent(&L.token_ranks[t], m);
-    write_token_layout<P, false>(L, t, p, m);
+    store_route<P, KS>(a, t, p, sel, wt);
   }
 
   if (!last_block_done(&L.sync->ticket, nblocks)) return false;
