@@ -103,10 +103,11 @@ __device__ __forceinline__ void list_insert(uint32_t (&lk)[KL], int (&li)[KL], u
 }
 
 // Offers the lane's V candidates (ids id0 + v) to the list: all of them, or
-// with `refill`, only those ordered after the lane's last pick (fk, fid).  A
-// rolled loop keeps the code small; the load two 16-byte chunks ahead is
-// issued before the current chunk is inserted (the empty asm keeps the
-// compiler from sinking it).  `row` must be readable for V values.
+// with `refill`, only those ordered after the lane's last pick (fk, fid).  Up
+// to 16 candidates (four 16-byte loads) are loaded at once; longer rows go
+// through a rolled loop that keeps the code small, with the load two 16-byte
+// chunks ahead issued before the current chunk is inserted (the empty asm
+// keeps the compiler from sinking it).  `row` must be readable for V values.
 template <int KL>
 __device__ __forceinline__ void list_fill(uint32_t (&lk)[KL], int (&li)[KL], const float* row, int V, bool vec4,
                                           int id0, bool live, bool refill, uint32_t fk, int fid) {
@@ -116,7 +117,19 @@ __device__ __forceinline__ void list_fill(uint32_t (&lk)[KL], int (&li)[KL], con
     if (refill) key = (key < fk || (key == fk && id > fid)) ? key : 0u;
     list_insert<KL>(lk, li, key, id);
   };
-  if (vec4) {
+  if (vec4 && V <= 16) {  // up to four 16-byte loads: all issued before the first is used
+    const u32x4* r4 = reinterpret_cast<const u32x4*>(row);
+    const int n4 = V >> 2;
+    u32x4 c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = r4[min(i, n4 - 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < n4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) offer(c[i][j], 4 * i + j);
+      }
+  } else if (vec4) {
     const u32x4* r4 = reinterpret_cast<const u32x4*>(row);
     const int n4 = V >> 2;
     u32x4 c0 = r4[0];
