@@ -27,7 +27,7 @@ namespace moe {
 constexpr int kLayoutBlock = MOE_LAYOUT_BLOCK;  // tokens per block, multi-block path
 constexpr int kFusedMaxTokens = 1024;  // up to this many tokens one block does everything
 constexpr int kFusedMaxChunks = kFusedMaxTokens / kWave;
-constexpr int kCountTile = 4096;  // chunk counts staged in LDS per pass of the finalisation
+constexpr int kCountTile = 8192;  // chunk counts staged in LDS per pass of the finalisation
 
 // Words at the start of the workspace that coordinate the blocks of one launch.
 // They are zero between calls: the caller zero-fills a new workspace once, and
@@ -64,6 +64,8 @@ struct LayoutArgs {
   uint64_t rank_magic;
   int T, k, E, R, NC, NB;
   int mask_words;           // 1: mask rows written as 32-bit words (R % 4 == 0, aligned)
+  int mask_shift;           // log2(R) when R is a power of two >= 4 and the rows start 16-byte
+                            // aligned: whole waves write their rows as 16-byte pieces; else -1
   int ids_vec4;             // 1: id rows read as 16-byte vectors (k % 4 == 0, 16-byte aligned)
 };
 
@@ -115,6 +117,52 @@ __device__ __forceinline__ void write_mask_row(const LayoutArgs& a, int t, uint6
     }
   } else {
     for (int r = 0; r < a.R; ++r) dst[r] = (uint8_t)((m >> r) & 1u);
+  }
+}
+
+// The is_token_in_rank rows of the 64 tokens [t0, t0 + 64) of one wave (those
+// below T), R = 2^mask_shift bytes each, as 16-byte pieces: lane l writes
+// pieces l, l + 64, ... of the wave's 64 R contiguous bytes, so each store
+// instruction covers 1 KiB, where one lane per token writing its own row
+// would touch a cache line per lane and instruction.  mw: the 64 tokens' rank
+// bitmasks in LDS, written by this wave before the call.
+__device__ __forceinline__ void write_wave_mask_rows(const LayoutArgs& a, int t0, int lane, const uint64_t* mw) {
+  const int sh = a.mask_shift;
+  const int nbytes = min(kWave, a.T - t0) << sh;  // a multiple of R >= 4
+  uint8_t* base = a.mask + ((size_t)t0 << sh);
+  for (int q = lane; (q << 4) < nbytes; q += kWave) {
+    const int b0 = q << 4;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int b = b0 + 4 * k;
+      const uint32_t nib = (uint32_t)(mw[b >> sh] >> (b & ((1 << sh) - 1))) & 0xfu;
+      w[k] = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+    }
+    if (b0 + 16 <= nbytes) {
+      *reinterpret_cast<u32x4*>(base + b0) = u32x4{w[0], w[1], w[2], w[3]};
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (b0 + 4 * k < nbytes) *reinterpret_cast<uint32_t*>(base + b0 + 4 * k) = w[k];
+    }
+  }
+}
+
+// Token t's outputs: its rank bitmask (plan) and its is_token_in_rank row,
+// either by its own lane or, with mask_shift >= 0, staged in mw (the wave's 64
+// masks in LDS) and written by the whole wave.  Every lane of the wave calls it.
+__device__ __forceinline__ void write_token_outputs(const LayoutArgs& a, int t, int lane, uint64_t m, uint64_t* mw) {
+  if (t < a.T) a.token_ranks[t] = m;
+  if (a.mask_shift >= 0) {
+    mw[lane] = m;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int t0 = t - lane;
+    if (t0 < a.T) write_wave_mask_rows(a, t0, lane, mw);
+  } else if (t < a.T) {
+    write_mask_row(a, t, m);
   }
 }
 
@@ -193,22 +241,19 @@ __device__ __forceinline__ void small_chunk_rows(const LayoutArgs& a, const int 
 
 // The whole layout in one block of at least ceil(T/64) waves (at most 16):
 // thread i owns token i, wave w chunk w; waves beyond the last chunk count
-// nothing.  hist: E ints of LDS.  Returns (in every thread) once the plan is
+// nothing.  hist: E ints of LDS; mstage: 64 u64 of LDS per wave.  Returns (in every thread) once the plan is
 // written; offs[r] then holds the segment offset of rank r and offs[64] the
 // number of receive rows.
 template <int KI>
 __device__ __forceinline__ void layout_one_block(const LayoutArgs& a, int* hist, int (*cnt)[kWave],
-                                                 int (*wave_cnt)[kWave], int* offs) {
+                                                 int (*wave_cnt)[kWave], int* offs, uint64_t* mstage) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   for (int e = tid; e < a.E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
 
   const uint64_t m = token_rank_mask<KI>(a, tid, hist);
-  if (tid < a.T) {
-    a.token_ranks[tid] = m;
-    write_mask_row(a, tid, m);
-  }
   cnt[wave][lane] = wave_rank_counts(m, a.R, lane, wave_cnt[wave]);
+  write_token_outputs(a, tid, lane, m, mstage + wave * kWave);
   __syncthreads();
 
   for (int e = tid; e < a.E; e += blockDim.x) a.tokens_per_expert[e] = hist[e];
@@ -224,7 +269,8 @@ __global__ __launch_bounds__(kFusedMaxTokens) void layout_fused_kernel(LayoutArg
   __shared__ int cnt[kFusedMaxChunks][kWave];
   __shared__ int wave_cnt[kFusedMaxChunks][kWave];
   __shared__ int offs[kWave + 1];
-  layout_one_block<KI>(a, hist, cnt, wave_cnt, offs);
+  __shared__ uint64_t mstage[kFusedMaxTokens];
+  layout_one_block<KI>(a, hist, cnt, wave_cnt, offs, mstage);
 }
 
 // Last-block-done.  Every wave of the block, having written with put_coherent
@@ -268,19 +314,24 @@ __device__ __forceinline__ void load_count_batch(const LayoutArgs& a, int (&v)[k
 // from the expert accumulator (both cleared for the next call), then the chunk
 // counts, kCountTile at a time, staged in LDS (tile), scanned per rank (one
 // wave per rank) and written back as receive rows.  The rank totals, the first
-// expert totals and the first batch of chunk counts are loaded together, so
-// shapes whose counts fit one batch take one round of loads.  offs: 64 ints of
-// LDS.  Every thread of the block must call it.
+// expert totals and the first tile's chunk counts (at most two batches of
+// loads per thread) are loaded together, so shapes whose counts fit one tile
+// take one round of loads.  offs: 64 ints of LDS.  Every thread of the block
+// must call it.
 __device__ __forceinline__ void finalize_chunk_rows(const LayoutArgs& a, int* tile, int* offs) {
   constexpr int kBatch = 16;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int nthreads = blockDim.x, nwaves = nthreads >> 6;
-  const int TC = kCountTile / a.R;  // chunks of every rank per tile (R <= 64: at least 64)
+  const int TC = kCountTile / a.R;  // chunks of every rank per tile (R <= 64: at least 128)
 
+  // the first tile: up to two batches of loads per thread, all issued before any is used
+  const int nc0 = min(TC, a.NC), n0 = a.R * nc0;
   const int rv = get_coherent(&a.rank_acc[min(lane, a.R - 1)]);
   const int ev = get_coherent(&a.expert_acc[min(tid, a.E - 1)]);
-  int v[kBatch];
-  load_count_batch<kBatch>(a, v, tid, nthreads, a.R * min(TC, a.NC), min(TC, a.NC), 0);
+  int v[kBatch], w[kBatch];
+  load_count_batch<kBatch>(a, v, tid, nthreads, n0, nc0, 0);
+  const bool two = n0 > kBatch * nthreads;  // block-uniform
+  if (two) load_count_batch<kBatch>(a, w, tid + kBatch * nthreads, nthreads, n0, nc0, 0);
 
   if (wave == 0) {
     offs[lane] = publish_rank_offsets(a, rv, lane);
@@ -293,10 +344,11 @@ __device__ __forceinline__ void finalize_chunk_rows(const LayoutArgs& a, int* ti
   for (int c0 = 0; c0 < a.NC; c0 += TC) {
     const int nc = min(TC, a.NC - c0), n = a.R * nc;
     for (int i0 = tid; i0 < n; i0 += kBatch * nthreads) {
-      if (c0 != 0 || i0 != tid) load_count_batch<kBatch>(a, v, i0, nthreads, n, nc, c0);
+      const bool first = c0 == 0 && i0 == tid, second = c0 == 0 && i0 == tid + kBatch * nthreads;
+      if (!first && !second) load_count_batch<kBatch>(a, v, i0, nthreads, n, nc, c0);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
-        if (i0 + u * nthreads < n) tile[i0 + u * nthreads] = v[u];
+        if (i0 + u * nthreads < n) tile[i0 + u * nthreads] = second ? w[u] : v[u];
     }
     __syncthreads();
     for (int r = wave; r < a.R; r += nwaves) {
@@ -319,10 +371,11 @@ __device__ __forceinline__ void finalize_chunk_rows(const LayoutArgs& a, int* ti
 // four chunks, rank and expert totals added to the accumulators -- and the
 // block that finishes last turns the counts into receive rows and returns true.
 // Every thread of the block must call it.  hist: E ints of LDS; tile:
-// kCountTile ints; offs: 64 ints.
+// kCountTile ints; offs: 64 ints; mstage: kLayoutBlock u64.
 template <int KI>
 __device__ __forceinline__ bool layout_count_produce(const LayoutArgs& a, int b, int nblocks, int* hist,
-                                                     int (*wave_cnt)[kWave], int* tile, int* offs) {
+                                                     int (*wave_cnt)[kWave], int* tile, int* offs,
+                                                     uint64_t* mstage) {
   constexpr int kChunks = kLayoutBlock / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   for (int e = tid; e < a.E; e += kLayoutBlock) hist[e] = 0;
@@ -342,10 +395,7 @@ __device__ __forceinline__ bool layout_count_produce(const LayoutArgs& a, int b,
   // The plain output stores come last: the compiler waits for outstanding
   // stores before reusing their registers, and here that wait is the one the
   // ticket needs anyway rather than a round trip of its own mid-block.
-  if (t < a.T) {
-    a.token_ranks[t] = m;
-    write_mask_row(a, t, m);
-  }
+  write_token_outputs(a, t, lane, m, mstage + wave * kWave);
 
   if (!last_block_done(&a.sync->ticket, nblocks)) return false;
   finalize_chunk_rows(a, tile, offs);
@@ -360,7 +410,8 @@ __global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(LayoutArgs a
   __shared__ int wave_cnt[kLayoutBlock / kWave][kWave];
   __shared__ int tile[kCountTile];
   __shared__ int offs[kWave];
-  layout_count_produce<KI>(a, blockIdx.x, gridDim.x, hist, wave_cnt, tile, offs);
+  __shared__ uint64_t mstage[kLayoutBlock];
+  layout_count_produce<KI>(a, blockIdx.x, gridDim.x, hist, wave_cnt, tile, offs, mstage);
 }
 
 }  // namespace moe

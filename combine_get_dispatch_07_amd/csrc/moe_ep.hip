@@ -326,6 +326,14 @@ void launch_router(int T, size_t lds, hipStream_t stream, const moe::RouterArgs&
   }
 }
 
+// log2(R) when R is a power of two >= 4 and is_token_in_rank is 16-byte aligned (a wave's rows are
+// then 16-byte aligned too: 64 R bytes per wave), else -1.
+int mask_shift(const moe_shape& s, const void* is_token_in_rank) {
+  const int R = s.num_ranks;
+  if (R < 4 || (R & (R - 1)) != 0 || !aligned(is_token_in_rank, 16)) return -1;
+  return __builtin_ctz((unsigned)R);
+}
+
 // Layout arguments after every check moe_get_dispatch_layout makes (shape already checked).
 moe_status layout_args(const moe_shape& s, const int32_t* topk_idx, int32_t* tokens_per_rank,
                        int32_t* tokens_per_expert, uint8_t* is_token_in_rank, void* workspace, size_t workspace_bytes,
@@ -360,6 +368,7 @@ moe_status layout_args(const moe_shape& s, const int32_t* topk_idx, int32_t* tok
   a.NC = p.NC;
   a.NB = p.NB;
   a.mask_words = (s.num_ranks % 4 == 0 && aligned(is_token_in_rank, 4)) ? 1 : 0;
+  a.mask_shift = mask_shift(s, is_token_in_rank);
   a.ids_vec4 = (s.num_topk % 4 == 0 && aligned(topk_idx, 16)) ? 1 : 0;
   return MOE_OK;
 }
@@ -533,6 +542,7 @@ moe_status route_args(const moe_shape& s, const moe_router* router, const float*
   a.lay.NC = p.NC;
   a.lay.NB = p.NC;  // one routing block per 64-token chunk
   a.lay.mask_words = (s.num_ranks % 4 == 0 && aligned(is_token_in_rank, 4)) ? 1 : 0;
+  a.lay.mask_shift = mask_shift(s, is_token_in_rank);
   a.lay.ids_vec4 = (k % 4 == 0 && aligned(topk_idx, 16)) ? 1 : 0;  // the layout kernel's reads of the ids
   a.V = E % 16 == 0 ? E / 16 : E / 8;  // experts per lane: 16 or 8 lanes per token
   a.G = G;

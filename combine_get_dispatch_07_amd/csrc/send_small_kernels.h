@@ -41,13 +41,14 @@ __global__ __launch_bounds__(kSendSmallMaxWaves * kWave) void send_small_kernel(
   __shared__ int wave_cnt[kFusedMaxChunks][kWave];
   __shared__ int rank_total[kWave + 1];  // layout block: offsets; token blocks: tokens per rank
   __shared__ int before[kWave];      // token blocks: tokens before t going to each rank
+  __shared__ uint64_t mstage[kFusedMaxTokens];  // layout block: the tokens' rank bitmasks
   const LayoutArgs& L = args.lay;
   const DispatchArgs& a = args.d;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   if (blockIdx.x == a.T) {  // the layout, then the dispatch's segment offsets and row count
-    layout_one_block<KI>(L, hist, chunk_cnt, wave_cnt, rank_total);
+    layout_one_block<KI>(L, hist, chunk_cnt, wave_cnt, rank_total, mstage);
     if (wave == 0) {
       if (lane < a.R) a.rank_offsets[lane] = rank_total[lane];
       if (lane == 0) {
