@@ -178,7 +178,10 @@ __device__ __forceinline__ void add_rank_bits(uint64_t m, int* cnt) {
 // is 64 ints of LDS private to the wave.  Up to kBallotRanks ranks: one ballot
 // per rank (scalar work, no LDS); above, one LDS atomic per set bit, where the
 // set bits of all lanes hit the same few counters far less often.
-constexpr int kBallotRanks = 16;
+#ifndef MOE_BALLOT_RANKS
+#define MOE_BALLOT_RANKS 16
+#endif
+constexpr int kBallotRanks = MOE_BALLOT_RANKS;
 __device__ __forceinline__ int wave_rank_counts(uint64_t m, int R, int lane, int* cnt) {
   if (R <= kBallotRanks) {
     int mine = 0;
@@ -351,16 +354,25 @@ __device__ __forceinline__ void finalize_chunk_rows(const LayoutArgs& a, int* ti
         if (i0 + u * nthreads < n) tile[i0 + u * nthreads] = second ? w[u] : v[u];
     }
     __syncthreads();
-    for (int r = wave; r < a.R; r += nwaves) {
-      int run = offs[r];
-      for (int j0 = 0; j0 < nc; j0 += kWave) {
-        const int j = j0 + lane;
-        const int c = j < nc ? tile[r * nc + j] : 0;
+    if (nc <= kWave) {  // one chunk per lane: one wave scan per rank
+      for (int r = wave; r < a.R; r += nwaves) {
+        const int c = lane < nc ? tile[r * nc + lane] : 0;
         const int incl = wave_inclusive_scan(c, lane);
-        if (j < nc) put_coherent(&a.chunk_base[r * a.NC + c0 + j], run + incl - c);
-        run += __builtin_amdgcn_readlane(incl, kWave - 1);
+        if (lane < nc) put_coherent(&a.chunk_base[r * a.NC + c0 + lane], offs[r] + incl - c);
+        if (lane == kWave - 1) offs[r] += incl;
       }
-      if (lane == 0) offs[r] = run;
+    } else {  // 64 chunks at a time, the carry between them through a readlane (contiguous stores)
+      for (int r = wave; r < a.R; r += nwaves) {
+        int run = offs[r];
+        for (int j0 = 0; j0 < nc; j0 += kWave) {
+          const int j = j0 + lane;
+          const int c = j < nc ? tile[r * nc + j] : 0;
+          const int incl = wave_inclusive_scan(c, lane);
+          if (j < nc) put_coherent(&a.chunk_base[r * a.NC + c0 + j], run + incl - c);
+          run += __builtin_amdgcn_readlane(incl, kWave - 1);
+        }
+        if (lane == 0) offs[r] = run;
+      }
     }
     __syncthreads();
   }
