@@ -244,9 +244,9 @@ __device__ __forceinline__ void small_chunk_rows(const LayoutArgs& a, const int 
 
 // The whole layout in one block of at least ceil(T/64) waves (at most 16):
 // thread i owns token i, wave w chunk w; waves beyond the last chunk count
-// nothing.  hist: E ints of LDS; mstage: 64 u64 of LDS per wave.  Returns (in every thread) once the plan is
-// written; offs[r] then holds the segment offset of rank r and offs[64] the
-// number of receive rows.
+// nothing.  hist: E ints of LDS; mstage: 64 u64 of LDS per wave.  Returns (in
+// every thread) once the plan is written; offs[r] then holds the segment
+// offset of rank r and offs[64] the number of receive rows.
 template <int KI>
 __device__ __forceinline__ void layout_one_block(const LayoutArgs& a, int* hist, int (*cnt)[kWave],
                                                  int (*wave_cnt)[kWave], int* offs, uint64_t* mstage) {
