@@ -47,7 +47,8 @@ def _results(lay, d, out):
 
 
 @pytest.mark.parametrize("name,T,routed", [("decode", 128, False), ("prefill", 2048, False), ("decode", 128, True),
-                                           ("prefill", 2048, True)])
+                                           ("prefill", 2048, True), ("group_limited", 2048, False),
+                                           ("skewed", 3000, False)])
 def test_graph_replays_match_eager(name, T, routed):
     import combine_get_dispatch_07_amd as moe
     from tests.gpu_harness import to_dev_bf16
