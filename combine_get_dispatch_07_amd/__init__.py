@@ -43,6 +43,8 @@ def alloc_route(shape: MoeShape, device="cuda") -> Dict[str, torch.Tensor]:
 
 def run_route(shape: MoeShape, logits: torch.Tensor, lay: Dict[str, torch.Tensor], gate: str = "softmax",
               num_groups: int = 1, topk_groups: int = 1, stream=None) -> None:
+    """moe_route_layout: top-k routing of `logits` [T, E] fp32 ("softmax" or "sigmoid" gate, optional
+    group limit) fused with the layout; fills lay's ids, weights, counts, mask and plan."""
     moe_route_layout(shape, logits, lay["topk_idx"], lay["topk_w"], lay["tokens_per_rank"], lay["tokens_per_expert"],
                      lay["is_token_in_rank"], lay["workspace"], gate, num_groups, topk_groups, stream)
 
@@ -65,12 +67,14 @@ def alloc_dispatch(shape: MoeShape, dtype: str, device="cuda", capacity: Optiona
 
 
 def run_layout(shape: MoeShape, topk_idx: torch.Tensor, lay: Dict[str, torch.Tensor], stream=None) -> None:
+    """moe_get_dispatch_layout: counts, is_token_in_rank and the dispatch plan into `lay`."""
     moe_get_dispatch_layout(shape, topk_idx, lay["tokens_per_rank"], lay["tokens_per_expert"],
                             lay["is_token_in_rank"], lay["workspace"], stream)
 
 
 def run_dispatch(shape: MoeShape, dtype: str, x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
                  lay: Dict[str, torch.Tensor], d: Dict[str, torch.Tensor], stream=None) -> None:
+    """moe_dispatch: rows of `x` packed into d's receive buffers, from the plan in lay["workspace"]."""
     moe_dispatch(shape, dtype, x, topk_idx, topk_w, lay["workspace"], d["recv_x"], d["recv_scales"],
                  d["recv_src_idx"], d["recv_topk_idx"], d["recv_topk_w"], d["rank_offsets"], d["send_row"],
                  d["num_recv"], stream)
@@ -144,5 +148,6 @@ def alloc_dispatch_ll(shape: MoeShape, dtype: str, device="cuda", capacity: Opti
 
 def run_dispatch_ll(shape: MoeShape, dtype: str, x: torch.Tensor, topk_idx: torch.Tensor,
                     d: Dict[str, torch.Tensor], stream=None) -> None:
+    """moe_dispatch_ll: one receive buffer per expert, positions and counts into `d`."""
     moe_dispatch_ll(shape, dtype, x, topk_idx, d["workspace"], d["recv_x"], d["recv_scales"], d["recv_src_idx"],
                     d["recv_count"], d["slot_pos"], stream)
